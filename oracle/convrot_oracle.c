@@ -1,0 +1,374 @@
+/*
+ * ConvRot W8A8 / W4A8 linear -- CPU ORACLE (test infrastructure only).
+ *
+ * This file is the plain, slow, obviously-correct definition of what the
+ * ConvRot quantized linear computes.  It exists so that tests, the smoke check
+ * and the benchmark's CPU-baseline leg can check the HIP library against it.
+ * It is NOT part of the product path: nothing in the library links, loads or
+ * calls it, and it shares no code, header, table or constant with the GPU
+ * kernels.
+ *
+ * Sources (web pages on ConvRot int8/int4 checkpoints):
+ *  [P1] "MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file table,
+ *       rows "Quantized" and "Matmul".
+ *  [P2] "qwen3.5_4b_int8_convrot", sections "Why ConvRot" and
+ *       "Quantization Recipe" (--scaling_mode row --simple, group size 256).
+ *  [P3] "qwen3vl_8b_int8_convrot", section "Layer and group selection".
+ *  [P4] "craftingmod/Qwen3-VL-8B-Heretic-INT8", section "Quantization metadata"
+ *       (convrot, convrot_groupsize 256, per_row, orig_dtype bfloat16).
+ *  [P5] "MossInt4", section "Format" (signed 4-bit codes two per byte, one F32
+ *       scale per row chosen by a clip search, 8-bit activations).
+ *
+ * Readings taken where the pages are silent (each one is listed with its
+ * reason in the design notes of the repository):
+ *  - Hadamard: Sylvester construction in natural order,
+ *    H[i][j] = (-1)^popcount(i & j) / sqrt(g); rotation is x' = x * H applied
+ *    to each contiguous group of g columns along K.  g = 1 means no rotation.
+ *  - Decision precision: the rotation is computed here in fp64 by an explicit
+ *    dense matrix product (not a fast transform); the rotated value is then
+ *    rounded to fp32 and every step that decides an integer code (absmax,
+ *    scale, quotient, rounding) is taken in fp32, the precision of the kernel.
+ *  - scale = absmax / 127 (fp32, correctly rounded); code =
+ *    round_half_away_from_zero(value / scale) clamped to [-127, 127]; an
+ *    all-zero row gets scale 0 and codes 0.
+ *  - GEMM: naive triple loop, exact integer accumulation.
+ *  - Epilogue: y = bf16_rne(((float)acc * s_x[m]) * s_w[n]) in fp32.
+ *  - int4: codes in [-7, 7]; clip factor c from 1.00 down to 0.50 in steps of
+ *    0.01; scale = c * absmax / 7; the c with the smallest sum of squared
+ *    reconstruction error wins (ties to the larger c); byte j of a row holds
+ *    column 2j in its low nibble and column 2j+1 in its high nibble.
+ *
+ * Build: gcc -std=c11 -O2 -fopenmp -ffp-contract=off -shared -fPIC.
+ * OpenMP is used only to run independent rows in parallel; every row is
+ * computed by the same sequential loop.
+ *
+ * parity: every function below is pinned by the CPU tests (closed forms,
+ * library routines, brute force on tiny inputs); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_OVERFLOW 2
+
+/* ---------------------------------------------------------------- helpers */
+
+/* bf16 bit pattern -> fp64, exact (bf16 is the top half of an fp32). */
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even.  The 16 dropped
+ * mantissa bits are compared with one half of the kept unit in the last
+ * place; NaN stays a quiet NaN. */
+static uint16_t float_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xffffu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))
+        kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* Round half away from zero (C's roundf is exactly this). */
+static float round_half_away(float v) { return roundf(v); }
+
+static int is_pow2(int64_t g) { return g > 0 && (g & (g - 1)) == 0; }
+
+/* ---------------------------------------------------------- the Hadamard */
+
+/* H[i*g + j] = (-1)^popcount(i & j) / sqrt(g), Sylvester order. */
+void oracle_hadamard(int g, double *H) {
+    double norm = 1.0 / sqrt((double)g);
+    for (int i = 0; i < g; ++i)
+        for (int j = 0; j < g; ++j)
+            H[(int64_t)i * g + j] = (__builtin_popcount((unsigned)(i & j)) & 1) ? -norm : norm;
+}
+
+/* Rotate one row of K values in fp64: for every group of g contiguous
+ * columns, out[j] = sum_i in[i] * H[i][j] (dense product, [P1] "Quantized"
+ * and "Matmul" rows: the same Hadamard rotates weight rows and inputs). */
+static void rotate_row_f64(const double *in, int64_t K, int g, const double *H, double *out) {
+    for (int64_t base = 0; base < K; base += g) {
+        for (int j = 0; j < g; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < g; ++i)
+                acc += in[base + i] * H[(int64_t)i * g + j];
+            out[base + j] = acc;
+        }
+    }
+}
+
+/* rows x K fp64 -> rotated fp64 (exposed for the identity tests). */
+int oracle_rotate_rows(const double *x, int64_t rows, int64_t K, int g, double *out) {
+    if (!x || !out || rows < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
+    if (!H) return ORACLE_ERR_ARG;
+    oracle_hadamard(g, H);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        rotate_row_f64(x + r * K, K, g, H, out + r * K);
+    free(H);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------- int8 row quantization */
+
+/* Quantize one rotated row (already rounded to fp32) with a symmetric int8
+ * grid: scale = absmax/127, code = round_half_away(v / scale).
+ * ([P1] "Quantized": int8 with one fp32 scale per output row; "Matmul": the
+ * input is rounded to int8 per token; [P2] "Quantization Recipe":
+ * --scaling_mode row --simple, i.e. plain rounding.) */
+static void quantize_row_i8(const float *v, int64_t K, int8_t *q, float *scale) {
+    float amax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(v[k]);
+        if (a > amax) amax = a;
+    }
+    /* fp32 / fp32 done in fp64 then rounded once more to fp32 equals the
+     * correctly rounded fp32 quotient (53 >= 2*24 + 2). */
+    float s = (float)((double)amax / 127.0);
+    *scale = s;
+    for (int64_t k = 0; k < K; ++k) {
+        if (s == 0.0f) { q[k] = 0; continue; }
+        float t = (float)((double)v[k] / (double)s);
+        float r = round_half_away(t);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        q[k] = (int8_t)r;
+    }
+}
+
+/* Weight preparation, int8: W fp32 [N,K] -> wq int8 [N,K], scale fp32 [N]. */
+int oracle_quantize_weight_i8(const float *w, int64_t N, int64_t K, int g, int8_t *wq, float *scale) {
+    if (!w || !wq || !scale || N < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
+    if (!H) return ORACLE_ERR_ARG;
+    oracle_hadamard(g, H);
+#pragma omp parallel
+    {
+        double *in = (double *)malloc(sizeof(double) * (size_t)K);
+        double *rot = (double *)malloc(sizeof(double) * (size_t)K);
+        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) in[k] = (double)w[n * K + k];
+            rotate_row_f64(in, K, g, H, rot);
+            for (int64_t k = 0; k < K; ++k) rot32[k] = (float)rot[k];
+            quantize_row_i8(rot32, K, wq + n * K, scale + n);
+        }
+        free(in); free(rot); free(rot32);
+    }
+    free(H);
+    return ORACLE_OK;
+}
+
+/* Activation rotate + per-token quantization: x bf16 [M,K] -> xq int8 [M,K],
+ * x_scale fp32 [M] ([P1] "Matmul" row). */
+int oracle_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int g, int8_t *xq, float *x_scale) {
+    if (!x || !xq || !x_scale || M < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
+    if (!H) return ORACLE_ERR_ARG;
+    oracle_hadamard(g, H);
+#pragma omp parallel
+    {
+        double *in = (double *)malloc(sizeof(double) * (size_t)K);
+        double *rot = (double *)malloc(sizeof(double) * (size_t)K);
+        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t m = 0; m < M; ++m) {
+            for (int64_t k = 0; k < K; ++k) in[k] = bf16_bits_to_double(x[m * K + k]);
+            rotate_row_f64(in, K, g, H, rot);
+            for (int64_t k = 0; k < K; ++k) rot32[k] = (float)rot[k];
+            quantize_row_i8(rot32, K, xq + m * K, x_scale + m);
+        }
+        free(in); free(rot); free(rot32);
+    }
+    free(H);
+    return ORACLE_OK;
+}
+
+/* ----------------------------------------------------------------- GEMM */
+
+/* acc[m,n] = sum_k xq[m,k] * wq[n,k] ([P1] intro: the matmuls run in int8,
+ * weights and activations).  Naive triple loop; the sum is kept in int64 and
+ * must fit int32. */
+int oracle_gemm_i8(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K, int32_t *acc) {
+    if (!xq || !wq || !acc || M < 0 || N < 0 || K <= 0) return ORACLE_ERR_ARG;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)xq[m * K + k] * (int64_t)wq[n * K + k];
+            if (s > INT32_MAX || s < INT32_MIN) bad = 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return bad ? ORACLE_ERR_OVERFLOW : ORACLE_OK;
+}
+
+/* y[m,n] = bf16_rne(((float)acc * x_scale[m]) * w_scale[n]); output dtype is
+ * the original bf16 ([P4] "Quantization metadata": orig_dtype bfloat16). */
+int oracle_epilogue(const int32_t *acc, const float *x_scale, const float *w_scale,
+                    int64_t M, int64_t N, uint16_t *y) {
+    if (!acc || !x_scale || !w_scale || !y || M < 0 || N < 0) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            float a = (float)acc[m * N + n];
+            float t = a * x_scale[m];
+            float r = t * w_scale[n];
+            y[m * N + n] = float_to_bf16_rne(r);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The whole W8A8 linear: rotate + quantize x, int8 GEMM, rescale to bf16. */
+int oracle_w8a8_linear(const uint16_t *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
+                       int64_t N, int g, uint16_t *y) {
+    if (!x || !wq || !w_scale || !y || M < 0 || N < 0 || K <= 0) return ORACLE_ERR_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    int8_t *xq = (int8_t *)malloc((size_t)(M * K));
+    float *xs = (float *)malloc(sizeof(float) * (size_t)M);
+    int32_t *acc = (int32_t *)malloc(sizeof(int32_t) * (size_t)(M * N));
+    int rc = (xq && xs && acc) ? ORACLE_OK : ORACLE_ERR_ARG;
+    if (rc == ORACLE_OK) rc = oracle_rotate_quant(x, M, K, g, xq, xs);
+    if (rc == ORACLE_OK) rc = oracle_gemm_i8(xq, wq, M, N, K, acc);
+    if (rc == ORACLE_OK) rc = oracle_epilogue(acc, xs, w_scale, M, N, y);
+    free(xq); free(xs); free(acc);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ int4 */
+
+/* Scale for clip candidate i (c = (100 - i) / 100, i = 0..50):
+ * s = c * absmax / 7, evaluated as absmax * (100 - i) / 700 in fp64 and
+ * rounded to fp32 ([P5] "Format": one F32 scale per row chosen by a clip
+ * search per row). */
+static float int4_candidate_scale(float amax, int i) {
+    return (float)((double)amax * (double)(100 - i) / 700.0);
+}
+
+/* Codes of a row for a given scale: round_half_away(v / s) clamped to
+ * [-7, 7] (signed 4-bit codes, [P5] "Format"). */
+static void int4_codes(const float *v, int64_t K, float s, int8_t *q) {
+    for (int64_t k = 0; k < K; ++k) {
+        if (s == 0.0f) { q[k] = 0; continue; }
+        float t = (float)((double)v[k] / (double)s);
+        float r = round_half_away(t);
+        if (r > 7.0f) r = 7.0f;
+        if (r < -7.0f) r = -7.0f;
+        q[k] = (int8_t)r;
+    }
+}
+
+/* Sum of squared reconstruction error of a row, in fp64. */
+static double int4_row_error(const float *v, int64_t K, float s, const int8_t *q) {
+    double e = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+        double d = (double)q[k] * (double)s - (double)v[k];
+        e += d * d;
+    }
+    return e;
+}
+
+/* Weight preparation, int4: W fp32 [N,K] -> wq4 uint8 [N,K/2] (two signed
+ * nibbles per byte, low nibble = even column), scale fp32 [N]; clip_index[n]
+ * (may be NULL) receives the winning candidate i (c = 1 - i/100). */
+int oracle_quantize_weight_i4(const float *w, int64_t N, int64_t K, int g, uint8_t *wq4, float *scale,
+                              int32_t *clip_index) {
+    if (!w || !wq4 || !scale || N < 0 || K <= 0 || (K & 1) || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
+    if (!H) return ORACLE_ERR_ARG;
+    oracle_hadamard(g, H);
+#pragma omp parallel
+    {
+        double *in = (double *)malloc(sizeof(double) * (size_t)K);
+        double *rot = (double *)malloc(sizeof(double) * (size_t)K);
+        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
+        int8_t *q = (int8_t *)malloc((size_t)K);
+        int8_t *best_q = (int8_t *)malloc((size_t)K);
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; ++n) {
+            for (int64_t k = 0; k < K; ++k) in[k] = (double)w[n * K + k];
+            rotate_row_f64(in, K, g, H, rot);
+            float amax = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                rot32[k] = (float)rot[k];
+                if (fabsf(rot32[k]) > amax) amax = fabsf(rot32[k]);
+            }
+            int best_i = 0;
+            double best_err = 0.0;
+            float best_s = 0.0f;
+            for (int i = 0; i <= 50; ++i) {
+                float s = int4_candidate_scale(amax, i);
+                int4_codes(rot32, K, s, q);
+                double e = int4_row_error(rot32, K, s, q);
+                if (i == 0 || e < best_err) {
+                    best_err = e; best_i = i; best_s = s;
+                    memcpy(best_q, q, (size_t)K);
+                }
+            }
+            scale[n] = best_s;
+            if (clip_index) clip_index[n] = best_i;
+            for (int64_t j = 0; j < K / 2; ++j) {
+                uint8_t lo = (uint8_t)best_q[2 * j] & 0x0fu;
+                uint8_t hi = (uint8_t)best_q[2 * j + 1] & 0x0fu;
+                wq4[n * (K / 2) + j] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+        free(in); free(rot); free(rot32); free(q); free(best_q);
+    }
+    free(H);
+    return ORACLE_OK;
+}
+
+/* Packed int4 [N,K/2] -> int8 codes [N,K]: each nibble read as a signed
+ * 4-bit two's-complement number (-8..7). */
+int oracle_unpack_i4(const uint8_t *wq4, int64_t N, int64_t K, int8_t *wq) {
+    if (!wq4 || !wq || N < 0 || K <= 0 || (K & 1)) return ORACLE_ERR_ARG;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < K / 2; ++j) {
+            uint8_t b = wq4[n * (K / 2) + j];
+            int lo = b & 0x0f, hi = b >> 4;
+            wq[n * K + 2 * j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+            wq[n * K + 2 * j + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* The W4A8 linear: int4 weights unpacked, then exactly the W8A8 path
+ * ([P5] "Format": computation runs with 8-bit activations). */
+int oracle_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *wq4, const float *w_scale,
+                       int64_t N, int g, uint16_t *y) {
+    if (!x || !wq4 || !w_scale || !y || M < 0 || N < 0 || K <= 0 || (K & 1)) return ORACLE_ERR_ARG;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    int8_t *wq = (int8_t *)malloc((size_t)(N * K));
+    int rc = wq ? oracle_unpack_i4(wq4, N, K, wq) : ORACLE_ERR_ARG;
+    if (rc == ORACLE_OK) rc = oracle_w8a8_linear(x, M, K, wq, w_scale, N, g, y);
+    free(wq);
+    return rc;
+}
+
+/* Number of OpenMP threads a parallel region here would use. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,92 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case below plants one slip in a copy of the oracle's C source (on the
+CPU, in a temporary directory), builds it, points the oracle binding at the
+broken copy and runs the pin tests from test_oracle.py against it: at least
+one pin must fail.  The real oracle is restored afterwards.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "convrot_oracle.c")
+
+MUTANTS = [
+    ("ties_to_even", "static float round_half_away(float v) { return roundf(v); }",
+     "static float round_half_away(float v) { return rintf(v); }"),
+    ("no_normalisation", "double norm = 1.0 / sqrt((double)g);", "double norm = 1.0;"),
+    ("wrong_hadamard_or", "(__builtin_popcount((unsigned)(i & j)) & 1)",
+     "(__builtin_popcount((unsigned)(i | j)) & 1)"),
+    ("permuted_columns", "acc += in[base + i] * H[(int64_t)i * g + j];",
+     "acc += in[base + i] * H[(int64_t)i * g + ((j + 1) % g)];"),
+    ("interleaved_groups", "out[base + j] = acc;", "out[base / g + (int64_t)j * (K / g)] = acc;"),
+    ("scale_over_128", "float s = (float)((double)amax / 127.0);", "float s = (float)((double)amax / 128.0);"),
+    ("max_not_absmax", "float a = fabsf(v[k]);", "float a = v[k];"),
+    ("forgot_rotation", "rot32[k] = (float)rot[k];", "rot32[k] = (float)in[k];"),
+    ("transposed_weight", "(int64_t)wq[n * K + k];", "(int64_t)wq[k * N + n];"),
+    ("epilogue_order", "float t = a * x_scale[m];\n            float r = t * w_scale[n];",
+     "float t = x_scale[m] * w_scale[n];\n            float r = a * t;"),
+    ("bf16_truncation", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u)))\n        kept += 1u;",
+     "(void)dropped;"),
+    ("nibble_order", "(uint8_t)(lo | (hi << 4));", "(uint8_t)(hi | (lo << 4));"),
+    ("int4_clamp_8", "if (r > 7.0f) r = 7.0f;", "if (r > 8.0f) r = 8.0f;"),
+    ("int4_divisor_8", "(double)(100 - i) / 700.0", "(double)(100 - i) / 800.0"),
+    ("no_sign_extension", "(int8_t)(lo >= 8 ? lo - 16 : lo);", "(int8_t)(lo);"),
+    ("int4_no_search", "for (int i = 0; i <= 50; ++i) {", "for (int i = 0; i <= 0; ++i) {"),
+]
+
+PIN_TESTS = [
+    "test_hadamard_is_scipy_sylvester", "test_hadamard_orthogonal_bit_exact",
+    "test_rotation_matches_blockwise_library_product", "test_rotation_groups_are_contiguous",
+    "test_rotation_one_hot_closed_form", "test_worked_one_hot", "test_worked_constant_group",
+    "test_worked_half_away_ties_rotated", "test_worked_identity_group_ties",
+    "test_codes_range_and_absmax_code", "test_scale_is_absmax_over_127",
+    "test_rotate_quant_brute_force_tiny", "test_quantize_weight_i8_brute_force_tiny",
+    "test_gemm_exact_vs_int64_matmul", "test_epilogue_vs_torch_bf16_cast",
+    "test_epilogue_order_and_bf16_ties", "test_epilogue_multiplies_token_scale_first",
+    "test_rotation_suppresses_outlier_error",
+    "test_unpack_all_256_bytes", "test_worked_nibble_order", "test_worked_int4_equal_magnitude",
+    "test_int4_clip_search_brute_force",
+]
+
+
+def _run_pin(name):
+    fn = getattr(pins, name)
+    import inspect
+    params = inspect.signature(fn).parameters
+    if "g" in params:  # parametrised over group sizes
+        for g in (2, 16, 256):
+            fn(oracle, g)
+    elif "oracle_mod" in params:
+        fn(oracle)
+    else:
+        fn()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_kill_mutant(name, old, new):
+    src = open(SRC).read()
+    assert old in src, f"mutation site for {name} not found in the oracle source"
+    with tempfile.TemporaryDirectory() as d:
+        csrc = os.path.join(d, "m.c")
+        lib = os.path.join(d, f"liboracle_{name}.so")
+        with open(csrc, "w") as f:
+            f.write(src.replace(old, new))
+        subprocess.run(["gcc", *oracle.CFLAGS, "-w", csrc, "-o", lib, "-lm"], check=True)
+        oracle.use_library(lib)
+        try:
+            killed_by = None
+            for t in PIN_TESTS:
+                try:
+                    _run_pin(t)
+                except Exception as e:  # any failure of a pin kills the mutant
+                    killed_by = f"{t}: {type(e).__name__}"
+                    break
+        finally:
+            oracle.use_library(None)
+    assert killed_by is not None, f"no pin detects mutant {name}"
