@@ -1,0 +1,175 @@
+/*
+ * convrot.h -- C ABI of the ConvRot W8A8 / W4A8 quantized linear for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: web pages on ConvRot int8/int4 checkpoints):
+ *  - "MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file table:
+ *    row "Quantized" -- every weight row is rotated per contiguous 256-column
+ *    group by a Hadamard matrix and stored int8 with one fp32 scale per output
+ *    row; row "Matmul" -- at run time the input is rotated by the same
+ *    Hadamard, rounded to int8 per token and multiplied in int8.
+ *  - "qwen3.5_4b_int8_convrot", "Quantization Recipe": row-wise scaling with
+ *    plain rounding (--scaling_mode row --simple), group size 256.
+ *  - "craftingmod/Qwen3-VL-8B-Heretic-INT8", "Quantization metadata":
+ *    convrot, convrot_groupsize 256, per_row, orig_dtype bfloat16.
+ *  - "MossInt4", "Format": signed 4-bit weight codes two per byte with one
+ *    F32 scale per row chosen by a clip search; 8-bit activations.
+ *
+ * Definitions used by every call (H is the Sylvester Hadamard matrix of
+ * order g in natural order, H[i][j] = (-1)^popcount(i&j) / sqrt(g); a row is
+ * rotated by multiplying each contiguous group of g columns by H):
+ *    scale      = absmax(rotated row) / 127                  (fp32)
+ *    code       = round_half_away_from_zero(rotated / scale)  (int8, |code| <= 127)
+ *    acc[m][n]  = sum_k xq[m][k] * wq[n][k]                    (exact int32)
+ *    y[m][n]    = bf16_rne(((float)acc[m][n] * x_scale[m]) * w_scale[n])
+ * An all-zero row gets scale 0 and all codes 0.  Every decision that yields a
+ * code (absmax, scale, quotient, rounding) is taken in fp32.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
+ *    values are passed as their raw 16-bit patterns (uint16_t).
+ *  - The caller owns every buffer and the stream.  The library never
+ *    allocates or frees device memory, keeps no pointer after returning and
+ *    has no mutable global state: calls on different streams may run
+ *    concurrently.
+ *  - Work is enqueued on `stream` (0 = the null stream) without any host
+ *    synchronisation; results are valid once the stream has reached them.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    non-zero status nothing has been written.  M == 0 (or N == 0) is a
+ *    successful no-op.
+ *  - Tensor pointers must be 16-byte aligned; scale pointers 4-byte aligned.
+ *  - Shapes: K % 16 == 0, K % group == 0, K <= CONVROT_MAX_K; int4 weights
+ *    additionally need K % 32 == 0.  group must be a power of two in
+ *    [1, 256]; group 1 means no rotation (plain row-wise int8).  Unlike the
+ *    converter described on "qwen3vl_8b_int8_convrot" ("Layer and group
+ *    selection"), the library never silently falls back to group 1 when K is
+ *    not a multiple of the group: it returns CONVROT_ERR_SHAPE.
+ */
+#ifndef CONVROT_H_
+#define CONVROT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CONVROT_MAX_K 32768
+
+/* Status codes returned by every entry point. */
+enum convrot_status {
+  CONVROT_OK = 0,
+  CONVROT_ERR_NULL = 1,      /* a required pointer is NULL */
+  CONVROT_ERR_SHAPE = 2,     /* M < 0, N <= 0, K <= 0, K % 16, K % group, K odd/%32 for int4, K too large */
+  CONVROT_ERR_GROUP = 3,     /* group is not a power of two in [1, 256] */
+  CONVROT_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
+  CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than convrot_workspace_size() */
+  CONVROT_ERR_DEVICE = 6,    /* the HIP runtime reported an error while enqueueing */
+  CONVROT_ERR_DTYPE = 7      /* unsupported w_dtype or bits value */
+};
+
+/* Weight dtypes accepted by convrot_quantize_weight. */
+enum convrot_wdtype { CONVROT_W_F32 = 0, CONVROT_W_BF16 = 1 };
+
+/*
+ * convrot_quantize_weight -- offline weight preparation.
+ * Rotates every row of w [N, K] per group and quantizes it per output row
+ * ("MOSS-Image ... INT8" page, file table, row "Quantized"; "MossInt4",
+ * "Format" for bits == 4).
+ *   w        : [N, K] weights, fp32 (w_dtype 0) or bf16 bits (w_dtype 1).
+ *   bits == 8: wq is int8 [N, K]; codes = round_half_away(rotated/scale),
+ *              scale = absmax/127 (round-to-nearest; "Quantization Recipe":
+ *              --simple).
+ *   bits == 4: wq is uint8 [N, K/2]; byte j of a row holds column 2j in its
+ *              low nibble and column 2j+1 in its high nibble, each a signed
+ *              4-bit code in [-7, 7]; the row scale is c*absmax/7 for the c in
+ *              {1.00, 0.99, ..., 0.50} (evaluated as absmax*(100-i)/700 in
+ *              fp64, rounded to fp32) that minimises the row's sum of squared
+ *              reconstruction error (fp64), ties to the larger c.
+ *   w_scale  : fp32 [N], written.
+ * Returns a convrot_status.
+ */
+int convrot_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, int group, int bits,
+                            void *wq, float *w_scale, hipStream_t stream);
+
+/*
+ * convrot_rotate_quant -- run-time activation rotation + per-token int8
+ * quantization ("MOSS-Image ... INT8" page, file table, row "Matmul").
+ *   x       : bf16 bits [M, K]  (read)
+ *   xq      : int8 [M, K]       (written)
+ *   x_scale : fp32 [M]          (written)
+ */
+int convrot_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int group, int8_t *xq, float *x_scale,
+                         hipStream_t stream);
+
+/*
+ * convrot_workspace_size -- bytes of device workspace convrot_w8a8_linear and
+ * convrot_w4a8_linear need for an [M, K] input: the int8 codes and the fp32
+ * token scales, each rounded up to 256 bytes.  Returns 0 for M <= 0 or K <= 0.
+ */
+size_t convrot_workspace_size(int64_t M, int64_t K);
+
+/*
+ * convrot_w8a8_linear -- the ConvRot W8A8 linear ("MOSS-Image ... INT8" page,
+ * file table, row "Matmul"): y = bf16(((xq . wq^T) * x_scale) * w_scale)
+ * where (xq, x_scale) = rotate_quant(x).
+ *   x        : bf16 bits [M, K]            (read)
+ *   wq       : int8 [N, K], rotated codes  (read; from convrot_quantize_weight, bits 8)
+ *   w_scale  : fp32 [N]                    (read)
+ *   y        : bf16 bits [M, N]            (written)
+ *   workspace: device buffer of at least convrot_workspace_size(M, K) bytes,
+ *              16-byte aligned; its contents are scratch.
+ */
+int convrot_w8a8_linear(const uint16_t *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
+                        int64_t N, int group, uint16_t *y, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * convrot_w4a8_linear -- the int4-weight / int8-activation variant ("MossInt4",
+ * "Format": computation runs with 8-bit activations).  Identical to
+ * convrot_w8a8_linear except that wq4 is uint8 [N, K/2] holding two signed
+ * 4-bit codes per byte (low nibble = even column); a nibble is read as a
+ * two's-complement value in [-8, 7].  Requires K % 32 == 0.
+ */
+int convrot_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *wq4, const float *w_scale,
+                        int64_t N, int group, uint16_t *y, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * convrot_gemm_i8 -- the integer product and rescale on already-quantized
+ * operands (the GEMM half of the linear, exposed so a caller can share one
+ * quantized input across several weights and check the int32 accumulators).
+ *   xq       : int8 [M, K]                     (read)
+ *   x_scale  : fp32 [M]                        (read; may be NULL if y is NULL)
+ *   wq       : int8 [N, K] (wbits 8) or uint8 [N, K/2] (wbits 4)   (read)
+ *   w_scale  : fp32 [N]                        (read; may be NULL if y is NULL)
+ *   acc_out  : int32 [M, N] accumulators       (written if not NULL)
+ *   y        : bf16 bits [M, N]                (written if not NULL)
+ * At least one of acc_out and y must be non-NULL.
+ */
+int convrot_gemm_i8(const int8_t *xq, const float *x_scale, const void *wq, int wbits, const float *w_scale,
+                    int64_t M, int64_t N, int64_t K, int32_t *acc_out, uint16_t *y, hipStream_t stream);
+
+/*
+ * convrot_quantize_weight_i4_clip -- convrot_quantize_weight(bits = 4) that
+ * also writes, per row, the index i of the winning clip candidate
+ * (c = 1 - i/100) into clip_index (int32 [N], device).  Same arguments and
+ * errors otherwise; exposed so the clip search can be checked row by row.
+ */
+int convrot_quantize_weight_i4_clip(const void *w, int w_dtype, int64_t N, int64_t K, int group, uint8_t *wq4,
+                                    float *w_scale, int32_t *clip_index, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *convrot_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int convrot_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H_ */

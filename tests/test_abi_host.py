@@ -1,0 +1,140 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+- every function include/convrot.h declares is exported by libconvrot.so and
+  bound by the Python module;
+- argument validation returns the documented status before any device work
+  (only invalid argument sets are passed, so nothing is ever enqueued).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import w8a8_quantized_linear_amd as cr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(cr.library_path()):
+        pytest.skip("libconvrot.so not built (run __graft_entry__.build())")
+    return cr.load()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("convrot_quantize_weight", "convrot_rotate_quant", "convrot_w8a8_linear", "convrot_w4a8_linear"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in convrot.h but not exported"
+    assert sorted(cr.exported_symbols()) == declared_functions()
+
+
+def test_status_strings_and_version(L):
+    for s in range(0, 8):
+        assert len(cr.convrot_status_string(s)) > 0
+    assert "unknown" in cr.convrot_status_string(99)
+    assert cr.convrot_version() >= 100
+
+
+def test_workspace_size(L):
+    assert cr.convrot_workspace_size(0, 4096) == 0
+    assert cr.convrot_workspace_size(2048, 4096) == 2048 * 4096 + 2048 * 4
+    ws = cr.convrot_workspace_size(3, 16)
+    assert ws == 256 + 256 and ws % 256 == 0
+
+
+# Fake device addresses: non-NULL and 16-byte aligned.  Every call below
+# fails validation, so they are never dereferenced.
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+D = ctypes.c_void_p(0x40000)
+E = ctypes.c_void_p(0x50000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = None
+S0 = ctypes.c_void_p(0)
+
+ERR = {"null": 1, "shape": 2, "group": 3, "align": 4, "ws": 5, "dtype": 7}
+
+
+def rq(x, M, K, g, q, s):
+    return cr.load().convrot_rotate_quant(x, M, K, g, q, s, S0)
+
+
+def lin8(x, M, K, w, ws, N, g, y, wsp, wsb):
+    return cr.load().convrot_w8a8_linear(x, M, K, w, ws, N, g, y, wsp, wsb, S0)
+
+
+def lin4(x, M, K, w, ws, N, g, y, wsp, wsb):
+    return cr.load().convrot_w4a8_linear(x, M, K, w, ws, N, g, y, wsp, wsb, S0)
+
+
+def qw(w, dt, N, K, g, bits, q, s):
+    return cr.load().convrot_quantize_weight(w, dt, N, K, g, bits, q, s, S0)
+
+
+def gemm(xq, xs, wq, wb, wsc, M, N, K, acc, y):
+    return cr.load().convrot_gemm_i8(xq, xs, wq, wb, wsc, M, N, K, acc, y, S0)
+
+
+def test_rotate_quant_validation(L):
+    assert rq(NUL, 4, 256, 256, B, C) == ERR["null"]
+    assert rq(A, 4, 256, 256, NUL, C) == ERR["null"]
+    assert rq(A, 4, 300, 256, B, C) == ERR["shape"]       # K % 16
+    assert rq(A, 4, 272, 256, B, C) == ERR["shape"]       # K % group
+    assert rq(A, 4, 65536, 256, B, C) == ERR["shape"]     # K too large
+    assert rq(A, -1, 256, 256, B, C) == ERR["shape"]
+    assert rq(A, 4, 256, 3, B, C) == ERR["group"]
+    assert rq(A, 4, 512, 512, B, C) == ERR["group"]
+    assert rq(A, 4, 256, 0, B, C) == ERR["group"]
+    assert rq(MIS, 4, 256, 256, B, C) == ERR["align"]
+    assert rq(A, 4, 256, 256, MIS, C) == ERR["align"]
+    assert rq(A, 4, 256, 256, B, ctypes.c_void_p(0x30002)) == ERR["align"]
+    assert rq(NUL, 0, 256, 256, NUL, NUL) == 0             # empty input: no-op
+
+
+def test_linear_validation(L):
+    need = cr.convrot_workspace_size(8, 512)
+    assert lin8(A, 8, 512, B, C, 64, 256, D, E, need - 1) == ERR["ws"]
+    assert lin8(A, 8, 512, B, C, 64, 256, D, NUL, need) == ERR["null"]
+    assert lin8(A, 8, 512, B, C, 0, 256, D, E, need) == ERR["shape"]
+    assert lin8(A, 8, 500, B, C, 64, 256, D, E, need) == ERR["shape"]
+    assert lin8(A, 8, 512, B, C, 64, 256, MIS, E, need) == ERR["align"]
+    assert lin8(A, 8, 512, B, C, 64, 256, D, MIS, need) == ERR["align"]
+    assert lin8(A, 8, 512, B, C, 64, 100, D, E, need) == ERR["group"]
+    assert lin4(A, 8, 528, B, C, 64, 16, D, E, need) == ERR["shape"]   # int4 needs K % 32
+    assert lin8(NUL, 0, 512, NUL, NUL, 64, 256, NUL, NUL, 0) == 0
+
+
+def test_quantize_weight_validation(L):
+    assert qw(A, 2, 8, 256, 256, 8, B, C) == ERR["dtype"]
+    assert qw(A, 0, 8, 256, 256, 5, B, C) == ERR["dtype"]
+    assert qw(A, 0, 8, 250, 256, 8, B, C) == ERR["shape"]
+    assert qw(A, 0, 8, 272, 16, 4, B, C) == ERR["shape"]   # int4, K % 32
+    assert qw(A, 0, -1, 256, 256, 8, B, C) == ERR["shape"]
+    assert qw(NUL, 0, 8, 256, 256, 8, B, C) == ERR["null"]
+    assert qw(A, 0, 8, 256, 256, 8, MIS, C) == ERR["align"]
+    assert qw(NUL, 0, 0, 256, 256, 8, NUL, NUL) == 0
+
+
+def test_gemm_validation(L):
+    assert gemm(A, B, C, 8, D, 4, 4, 64, NUL, NUL) == ERR["null"]     # no output requested
+    assert gemm(A, NUL, C, 8, D, 4, 4, 64, NUL, E) == ERR["null"]     # y needs scales
+    assert gemm(A, B, C, 3, D, 4, 4, 64, E, NUL) == ERR["dtype"]
+    assert gemm(A, B, C, 8, D, 4, 0, 64, E, NUL) == ERR["shape"]
+    assert gemm(A, B, C, 4, D, 4, 4, 48, E, NUL) == ERR["shape"]
+    assert gemm(A, B, C, 8, D, 4, 4, 64, MIS, NUL) == ERR["align"]
+    assert gemm(NUL, NUL, NUL, 8, NUL, 0, 4, 64, NUL, NUL) == 0

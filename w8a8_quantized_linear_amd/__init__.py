@@ -1,1 +1,248 @@
-"""placeholder"""
+"""ConvRot W8A8 / W4A8 quantized linear for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/convrot.h`` (``libconvrot.so``,
+hand-written HIP kernels).  This module only marshals arguments: torch is used
+for device memory and the current stream, every step of the computation runs
+in the library's kernels.  There is no CPU fallback: if the library is not
+built, or no GPU is visible, every call raises.
+
+The functions named ``convrot_*`` mirror the C entry points one to one
+(device pointers as tensors, same argument order); the short names below them
+(``quantize_weight``, ``rotate_quant``, ``w8a8_linear``, ...) allocate the
+outputs and return them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "load", "library_path", "ConvRotError",
+    "convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
+    "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
+    "convrot_status_string", "convrot_version",
+    "quantize_weight", "rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8", "workspace",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libconvrot.so")
+_lib = None
+
+OK = 0
+W_F32, W_BF16 = 0, 1
+MAX_K = 32768
+
+
+class ConvRotError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status}: {text}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libconvrot.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m w8a8_quantized_linear_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sigs = {
+        "convrot_quantize_weight": (I, [P, I, I64, I64, I, I, P, P, P]),
+        "convrot_quantize_weight_i4_clip": (I, [P, I, I64, I64, I, P, P, P, P]),
+        "convrot_rotate_quant": (I, [P, I64, I64, I, P, P, P]),
+        "convrot_workspace_size": (SZ, [I64, I64]),
+        "convrot_w8a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
+        "convrot_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
+        "convrot_gemm_i8": (I, [P, P, P, I, P, I64, I64, I64, P, P, P]),
+        "convrot_status_string": (ctypes.c_char_p, [I]),
+        "convrot_version": (I, []),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    """Names the binding expects the library to export."""
+    return ["convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
+            "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
+            "convrot_status_string", "convrot_version"]
+
+
+# ------------------------------------------------------------ marshalling
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dptr(t):
+    """Device pointer of a tensor (None -> NULL); the tensor must be on a GPU."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("convrot: tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("convrot: tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _bits16(t):
+    """bf16 tensor -> same storage viewed as int16 (raw bit patterns)."""
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.int16, torch.uint16):
+        return t
+    raise TypeError(f"convrot: expected a bfloat16 tensor, got {t.dtype}")
+
+
+def _check(fn: str, rc: int):
+    if rc != OK:
+        raise ConvRotError(fn, rc, convrot_status_string(rc))
+
+
+# --------------------------------------------- C entry points, same names
+
+def convrot_status_string(status: int) -> str:
+    return load().convrot_status_string(int(status)).decode()
+
+
+def convrot_version() -> int:
+    return int(load().convrot_version())
+
+
+def convrot_workspace_size(M: int, K: int) -> int:
+    return int(load().convrot_workspace_size(int(M), int(K)))
+
+
+def convrot_quantize_weight(w, w_dtype, N, K, group, bits, wq, w_scale, stream=None) -> int:
+    return load().convrot_quantize_weight(_dptr(w), int(w_dtype), int(N), int(K), int(group), int(bits),
+                                          _dptr(wq), _dptr(w_scale), _stream(stream))
+
+
+def convrot_quantize_weight_i4_clip(w, w_dtype, N, K, group, wq4, w_scale, clip_index, stream=None) -> int:
+    return load().convrot_quantize_weight_i4_clip(_dptr(w), int(w_dtype), int(N), int(K), int(group),
+                                                  _dptr(wq4), _dptr(w_scale), _dptr(clip_index),
+                                                  _stream(stream))
+
+
+def convrot_rotate_quant(x, M, K, group, xq, x_scale, stream=None) -> int:
+    return load().convrot_rotate_quant(_dptr(x), int(M), int(K), int(group), _dptr(xq), _dptr(x_scale),
+                                       _stream(stream))
+
+
+def convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    return load().convrot_w8a8_linear(_dptr(x), int(M), int(K), _dptr(wq), _dptr(w_scale), int(N), int(group),
+                                      _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    return load().convrot_w4a8_linear(_dptr(x), int(M), int(K), _dptr(wq4), _dptr(w_scale), int(N), int(group),
+                                      _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc_out, y, stream=None) -> int:
+    return load().convrot_gemm_i8(_dptr(xq), _dptr(x_scale), _dptr(wq), int(wbits), _dptr(w_scale), int(M),
+                                  int(N), int(K), _dptr(acc_out), _dptr(y), _stream(stream))
+
+
+# ----------------------------------------------------- allocating helpers
+
+def quantize_weight(w, group: int = 256, bits: int = 8, with_clip_index: bool = False):
+    """w fp32/bf16 [N, K] on the GPU -> (wq, w_scale[, clip_index]).
+    bits 8: wq int8 [N, K]; bits 4: wq uint8 [N, K/2] (two nibbles per byte)."""
+    torch = _torch()
+    N, K = w.shape
+    if w.dtype == torch.float32:
+        wd = W_F32
+    elif w.dtype == torch.bfloat16:
+        wd = W_BF16
+    else:
+        raise TypeError("convrot.quantize_weight: w must be float32 or bfloat16")
+    dev = w.device
+    scale = torch.empty((N,), dtype=torch.float32, device=dev)
+    if bits == 8:
+        wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+    else:
+        wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    if bits == 4 and with_clip_index:
+        ci = torch.empty((N,), dtype=torch.int32, device=dev)
+        _check("convrot_quantize_weight_i4_clip",
+               convrot_quantize_weight_i4_clip(w, wd, N, K, group, wq, scale, ci))
+        return wq, scale, ci
+    _check("convrot_quantize_weight", convrot_quantize_weight(w, wd, N, K, group, bits, wq, scale))
+    return wq, scale
+
+
+def rotate_quant(x, group: int = 256):
+    """x bf16 [M, K] -> (xq int8 [M, K], x_scale fp32 [M])."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("convrot_rotate_quant", convrot_rotate_quant(x, M, K, group, xq, xs))
+    return xq, xs
+
+
+def workspace(M: int, K: int, device="cuda"):
+    torch = _torch()
+    n = convrot_workspace_size(M, K)
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
+
+
+def w8a8_linear(x, wq, w_scale, group: int = 256, out=None, ws=None):
+    """y = ConvRot W8A8 linear(x); x bf16 [M, K], wq int8 [N, K] -> y bf16 [M, N]."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    N = wq.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(M, K, x.device)
+    _check("convrot_w8a8_linear",
+           convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, ws, ws.numel()))
+    return y
+
+
+def w4a8_linear(x, wq4, w_scale, group: int = 256, out=None, ws=None):
+    """W4A8 variant; wq4 uint8 [N, K/2] -> y bf16 [M, N]."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    N = wq4.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = workspace(M, K, x.device)
+    _check("convrot_w4a8_linear",
+           convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, ws, ws.numel()))
+    return y
+
+
+def gemm_i8(xq, x_scale, wq, w_scale, wbits: int = 8, want_acc: bool = True, want_y: bool = True):
+    """Integer product on given codes -> (acc int32 [M, N] or None, y bf16 [M, N] or None)."""
+    torch = _torch()
+    M, K = xq.shape
+    N = wq.shape[0]
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if want_y else None
+    _check("convrot_gemm_i8", convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc, y))
+    return acc, y

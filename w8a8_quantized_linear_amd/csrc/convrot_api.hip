@@ -1,0 +1,145 @@
+// C-ABI layer: argument validation, workspace layout and kernel launches.
+// Validation runs on the host before anything is enqueued, so a non-zero
+// status means nothing was written.
+#include "../../include/convrot.h"
+
+#include "convrot_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int log2_group(int group) {
+  if (group < 1 || group > 256 || (group & (group - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < group) ++l;
+  return l;
+}
+
+// Shape rules shared by every call that rotates or multiplies along K.
+int check_k(int64_t K, int group, bool int4) {
+  if (log2_group(group) < 0) return CONVROT_ERR_GROUP;
+  if (K <= 0 || K % 16 != 0 || K % group != 0 || K > CONVROT_MAX_K) return CONVROT_ERR_SHAPE;
+  if (int4 && K % 32 != 0) return CONVROT_ERR_SHAPE;
+  return CONVROT_OK;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int convrot_version(void) { return 100; }
+
+const char* convrot_status_string(int status) {
+  switch (status) {
+    case CONVROT_OK: return "ok";
+    case CONVROT_ERR_NULL: return "a required pointer is NULL";
+    case CONVROT_ERR_SHAPE: return "invalid shape (need M >= 0, N > 0, K > 0, K % 16 == 0, K % group == 0, "
+                                   "K <= 32768, and K % 32 == 0 for int4 weights)";
+    case CONVROT_ERR_GROUP: return "group must be a power of two in [1, 256]";
+    case CONVROT_ERR_ALIGN: return "tensor pointers must be 16-byte aligned (scales 4-byte aligned)";
+    case CONVROT_ERR_WORKSPACE: return "workspace smaller than convrot_workspace_size(M, K)";
+    case CONVROT_ERR_DEVICE: return "the HIP runtime reported an error";
+    case CONVROT_ERR_DTYPE: return "unsupported weight dtype or bit width";
+    default: return "unknown convrot status";
+  }
+}
+
+size_t convrot_workspace_size(int64_t M, int64_t K) {
+  if (M <= 0 || K <= 0) return 0;
+  return round_up(size_t(M) * size_t(K), kAlign) + round_up(size_t(M) * sizeof(float), kAlign);
+}
+
+int convrot_quantize_weight(const void* w, int w_dtype, int64_t N, int64_t K, int group, int bits, void* wq,
+                            float* w_scale, hipStream_t stream) {
+  if (w_dtype != CONVROT_W_F32 && w_dtype != CONVROT_W_BF16) return CONVROT_ERR_DTYPE;
+  if (bits != 8 && bits != 4) return CONVROT_ERR_DTYPE;
+  if (int rc = check_k(K, group, bits == 4)) return rc;
+  if (N < 0) return CONVROT_ERR_SHAPE;
+  if (N == 0) return CONVROT_OK;
+  if (!w || !wq || !w_scale) return CONVROT_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
+  const int lg = log2_group(group);
+  if (bits == 8)
+    return device_status(convrot::launch_rotate_quant(w, w_dtype, N, K, lg, static_cast<int8_t*>(wq), w_scale,
+                                                      stream));
+  return device_status(convrot::launch_quantize_weight_i4(w, w_dtype, N, K, lg, static_cast<uint8_t*>(wq),
+                                                          w_scale, nullptr, stream));
+}
+
+// Same as convrot_quantize_weight(bits = 4) but also reports the winning clip
+// candidate per row (c = 1 - index/100); used by the tests.
+int convrot_quantize_weight_i4_clip(const void* w, int w_dtype, int64_t N, int64_t K, int group, uint8_t* wq4,
+                                    float* w_scale, int32_t* clip_index, hipStream_t stream) {
+  if (w_dtype != CONVROT_W_F32 && w_dtype != CONVROT_W_BF16) return CONVROT_ERR_DTYPE;
+  if (int rc = check_k(K, group, true)) return rc;
+  if (N < 0) return CONVROT_ERR_SHAPE;
+  if (N == 0) return CONVROT_OK;
+  if (!w || !wq4 || !w_scale || !clip_index) return CONVROT_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(wq4, 16) || !aligned(w_scale, 4) || !aligned(clip_index, 4))
+    return CONVROT_ERR_ALIGN;
+  return device_status(convrot::launch_quantize_weight_i4(w, w_dtype, N, K, log2_group(group), wq4, w_scale,
+                                                          clip_index, stream));
+}
+
+int convrot_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group, int8_t* xq, float* x_scale,
+                         hipStream_t stream) {
+  if (int rc = check_k(K, group, false)) return rc;
+  if (M < 0) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !xq || !x_scale) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return CONVROT_ERR_ALIGN;
+  return device_status(
+      convrot::launch_rotate_quant(x, CONVROT_W_BF16, M, K, log2_group(group), xq, x_scale, stream));
+}
+
+int convrot_gemm_i8(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,
+                    int64_t M, int64_t N, int64_t K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
+  if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || K > CONVROT_MAX_K || (wbits == 4 && K % 32 != 0))
+    return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!xq || !wq || (!acc_out && !y)) return CONVROT_ERR_NULL;
+  if (y && (!x_scale || !w_scale)) return CONVROT_ERR_NULL;
+  if (!aligned(xq, 16) || !aligned(wq, 16) || (acc_out && !aligned(acc_out, 16)) || (y && !aligned(y, 16)) ||
+      (x_scale && !aligned(x_scale, 4)) || (w_scale && !aligned(w_scale, 4)))
+    return CONVROT_ERR_ALIGN;
+  return device_status(convrot::launch_gemm(xq, x_scale, wq, wbits, w_scale, M, N, K, acc_out, y, stream));
+}
+
+static int linear_impl(const uint16_t* x, int64_t M, int64_t K, const void* wq, int wbits, const float* w_scale,
+                       int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  if (int rc = check_k(K, group, wbits == 4)) return rc;
+  if (M < 0 || N <= 0) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !wq || !w_scale || !y || !workspace) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
+  if (!aligned(workspace, 16)) return CONVROT_ERR_ALIGN;
+  if (workspace_bytes < convrot_workspace_size(M, K)) return CONVROT_ERR_WORKSPACE;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(size_t(M) * size_t(K), kAlign));
+  hipError_t e = convrot::launch_rotate_quant(x, CONVROT_W_BF16, M, K, log2_group(group), xq, xs, stream);
+  if (e != hipSuccess) return CONVROT_ERR_DEVICE;
+  return device_status(convrot::launch_gemm(xq, xs, wq, wbits, w_scale, M, N, K, nullptr, y, stream));
+}
+
+int convrot_w8a8_linear(const uint16_t* x, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
+                        int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return linear_impl(x, M, K, wq, 8, w_scale, N, group, y, workspace, workspace_bytes, stream);
+}
+
+int convrot_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wq4, const float* w_scale,
+                        int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  return linear_impl(x, M, K, wq4, 4, w_scale, N, group, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

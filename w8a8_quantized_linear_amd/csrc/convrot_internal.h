@@ -1,0 +1,24 @@
+// Internal launchers shared between the C-ABI layer and the kernel files.
+// Every launcher assumes its arguments were validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// x bf16 [rows, K] (in_dtype 1) or fp32 (in_dtype 0) -> codes int8 [rows, K]
+// with |code| <= qmax and fp32 scale [rows].  log2g = log2(group size).
+hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g,
+                               int8_t* codes, float* scale, hipStream_t stream);
+
+// int4 weight preparation with the per-row clip search; clip_index may be null.
+hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,
+                                     uint8_t* wq4, float* scale, int32_t* clip_index, hipStream_t stream);
+
+// acc = xq . wq^T (int32), optional bf16 epilogue.  wbits 8 or 4.
+hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits,
+                       const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t* acc_out,
+                       uint16_t* y, hipStream_t stream);
+
+}  // namespace convrot

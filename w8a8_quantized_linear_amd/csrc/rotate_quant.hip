@@ -1,0 +1,309 @@
+// Fused group-wise Hadamard rotation + per-row quantization on gfx950.
+//
+// One row (an activation token, or an output row of a weight) is held in the
+// registers of TPT threads; every thread owns C chunks of 16 consecutive
+// elements (chunk c = t + TPT * j).  A group of g <= 256 elements is g/16
+// consecutive chunks, so it sits in g/16 consecutive lanes of one 16-lane row
+// of the wavefront.  The fast Walsh-Hadamard transform then runs as:
+//   - stages over element-index bits 0..3: butterflies inside a thread's 16
+//     registers;
+//   - stages over bits 4..7: butterflies between lanes t and t ^ (1 << b-4)
+//     (cross-lane exchange within the 16-lane row).
+// The transform is left unnormalised (sums of +-x); for even log2(g) the 1/sqrt(g)
+// is a power of two and is folded exactly into the scale, for odd log2(g) it
+// is applied per element.
+//
+// The row's absmax is reduced across the TPT threads (wave shuffles, then LDS
+// across waves), after which every code is decided in fp32:
+//   scale = absmax / 127,  code = round_half_away(value / scale)
+// as stated for ConvRot int8 checkpoints ("MOSS-Image Qwen3.5-9B text encoder,
+// INT8 (W8A8, ConvRot)", file table rows "Quantized" and "Matmul").
+//
+// MODE_I4 runs the int4 weight preparation of "MossInt4" ("Format"): the same
+// rotation, then a per-row clip search over c = 1.00 .. 0.50 with fp64 error
+// sums, codes in [-7, 7] packed two per byte (low nibble = even column).
+#include "convrot_internal.h"
+
+#include <math.h>
+
+namespace convrot {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+enum { IN_F32 = 0, IN_BF16 = 1 };
+enum { MODE_I8 = 0, MODE_I4 = 1 };
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+template <int IN>
+__device__ __forceinline__ void load_chunk(const void* base, int64_t elem_off, float (&v)[16]) {
+  if constexpr (IN == IN_BF16) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem_off);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem_off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  }
+}
+
+// Butterflies over element bits 0..min(log2g, 4)-1 inside one chunk.
+__device__ __forceinline__ void fwht_in_register(float (&v)[16], int log2g) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b < log2g) {
+      const int h = 1 << b;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (!(i & h)) {
+          float a = v[i], c = v[i + h];
+          v[i] = a + c;
+          v[i + h] = a - c;
+        }
+      }
+    }
+  }
+}
+
+// Butterflies over element bits 4..log2g-1: partner lane differs in bit b-4.
+__device__ __forceinline__ void fwht_cross_lane(float (&v)[16], int log2g, int lane) {
+#pragma unroll
+  for (int b = 4; b < 8; ++b) {
+    if (b < log2g) {
+      const int m = 1 << (b - 4);
+      const bool high = (lane & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = __shfl_xor(v[i], m);
+        v[i] = high ? (p - v[i]) : (v[i] + p);
+      }
+    }
+  }
+}
+
+template <int TPT>
+__device__ __forceinline__ float row_max(float v, float* red) {
+  constexpr int kIn = TPT < 64 ? TPT : 64;
+#pragma unroll
+  for (int off = kIn / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if constexpr (TPT > 64) {
+    const int wave = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    const int first = (threadIdx.x / TPT) * (TPT / 64);
+    float r = red[first];
+#pragma unroll
+    for (int w = 1; w < TPT / 64; ++w) r = fmaxf(r, red[first + w]);
+    __syncthreads();
+    v = r;
+  }
+  return v;
+}
+
+template <int TPT>
+__device__ __forceinline__ double row_sum(double v, double* red) {
+  constexpr int kIn = TPT < 64 ? TPT : 64;
+#pragma unroll
+  for (int off = kIn / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if constexpr (TPT > 64) {
+    const int wave = threadIdx.x / 64;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    const int first = (threadIdx.x / TPT) * (TPT / 64);
+    double r = red[first];
+#pragma unroll
+    for (int w = 1; w < TPT / 64; ++w) r += red[first + w];
+    __syncthreads();
+    v = r;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
+         ((uint32_t(d) & 0xffu) << 24);
+}
+
+template <int TPT, int C, int IN, int MODE>
+__global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __restrict__ x, int64_t rows,
+                                                                int64_t K, int log2g, float inv_sqrt_g,
+                                                                float pow2_norm, void* __restrict__ codes,
+                                                                float* __restrict__ scale,
+                                                                int32_t* __restrict__ clip_index) {
+  constexpr int P = kThreads / TPT;  // rows per workgroup
+  __shared__ float red_f[kWaves];
+  __shared__ double red_d[kWaves];
+
+  const int t = threadIdx.x % TPT;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * P + threadIdx.x / TPT;
+  const bool row_ok = row < rows;
+  const int64_t nchunks = K / 16;
+  const bool odd = (log2g & 1) != 0;
+
+  float v[C][16];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int64_t c = t + int64_t(TPT) * j;
+    if (row_ok && c < nchunks) {
+      load_chunk<IN>(x, row * K + c * 16, v[j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[j][i] = 0.f;
+    }
+  }
+
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    fwht_in_register(v[j], log2g);
+    fwht_cross_lane(v[j], log2g, lane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (odd) v[j][i] *= inv_sqrt_g;
+      amax = fmaxf(amax, fabsf(v[j][i]));
+    }
+  }
+  amax = row_max<TPT>(amax, red_f);
+
+  if constexpr (MODE == MODE_I8) {
+    // v holds rotated values times 1/pow2_norm (exact power of two), so
+    // value/scale is the same quotient as v / (amax_v / 127).
+    const float s_v = amax / 127.0f;
+    if (row_ok && t == 0) scale[row] = s_v * pow2_norm;
+    int8_t* out = static_cast<int8_t*>(codes);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t c = t + int64_t(TPT) * j;
+      int q[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float r = (s_v == 0.f) ? 0.f : roundf(v[j][i] / s_v);
+        r = fminf(fmaxf(r, -127.f), 127.f);
+        q[i] = int(r);
+      }
+      if (row_ok && c < nchunks) {
+        uint4 o;
+        o.x = pack4_i8(q[0], q[1], q[2], q[3]);
+        o.y = pack4_i8(q[4], q[5], q[6], q[7]);
+        o.z = pack4_i8(q[8], q[9], q[10], q[11]);
+        o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+        *reinterpret_cast<uint4*>(out + row * K + c * 16) = o;
+      }
+    }
+  } else {
+    // int4 clip search on the normalised rotated values.
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[j][i] *= pow2_norm;
+    const float amax_n = amax * pow2_norm;
+    int best_i = 0;
+    double best_e = 0.0;
+    float best_s = 0.f;
+    for (int ci = 0; ci <= 50; ++ci) {
+      const float s = float(double(amax_n) * double(100 - ci) / 700.0);
+      double e = 0.0;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float r = (s == 0.f) ? 0.f : roundf(v[j][i] / s);
+          r = fminf(fmaxf(r, -7.f), 7.f);
+          double d = double(r) * double(s) - double(v[j][i]);
+          e += d * d;
+        }
+      }
+      e = row_sum<TPT>(e, red_d);
+      if (ci == 0 || e < best_e) {
+        best_e = e;
+        best_i = ci;
+        best_s = s;
+      }
+    }
+    if (row_ok && t == 0) {
+      scale[row] = best_s;
+      if (clip_index) clip_index[row] = best_i;
+    }
+    uint8_t* out = static_cast<uint8_t*>(codes);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t c = t + int64_t(TPT) * j;
+      uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float r = (best_s == 0.f) ? 0.f : roundf(v[j][i] / best_s);
+        r = fminf(fmaxf(r, -7.f), 7.f);
+        packed[i / 8] |= (uint32_t(int(r)) & 0xfu) << (4 * (i % 8));
+      }
+      if (row_ok && c < nchunks) {
+        *reinterpret_cast<uint2*>(out + row * (K / 2) + c * 8) = make_uint2(packed[0], packed[1]);
+      }
+    }
+  }
+}
+
+template <int IN, int MODE>
+hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* codes, float* scale,
+                    int32_t* clip_index, hipStream_t stream) {
+  const int64_t nchunks = K / 16;
+  const float inv_sqrt_g = float(1.0 / sqrt(double(1 << log2g)));
+  const float pow2_norm = (log2g & 1) ? 1.0f : ldexpf(1.0f, -(log2g / 2));
+  int tpt = 256, c = 1;
+  if (nchunks <= 256) {
+    tpt = 16;
+    while (tpt < nchunks) tpt *= 2;
+  } else {
+    c = int((nchunks + 255) / 256);
+  }
+  const int per_block = kThreads / tpt;
+  const dim3 grid(unsigned((rows + per_block - 1) / per_block));
+#define CONVROT_RQ(TPT_, C_)                                                                          \
+  hipLaunchKernelGGL((rotate_quant_kernel<TPT_, C_, IN, MODE>), grid, dim3(kThreads), 0, stream, x, rows, K, \
+                     log2g, inv_sqrt_g, pow2_norm, codes, scale, clip_index)
+  switch (tpt * 16 + c) {
+    case 16 * 16 + 1: CONVROT_RQ(16, 1); break;
+    case 32 * 16 + 1: CONVROT_RQ(32, 1); break;
+    case 64 * 16 + 1: CONVROT_RQ(64, 1); break;
+    case 128 * 16 + 1: CONVROT_RQ(128, 1); break;
+    case 256 * 16 + 1: CONVROT_RQ(256, 1); break;
+    case 256 * 16 + 2: CONVROT_RQ(256, 2); break;
+    case 256 * 16 + 3: CONVROT_RQ(256, 3); break;
+    case 256 * 16 + 4: CONVROT_RQ(256, 4); break;
+    case 256 * 16 + 5: CONVROT_RQ(256, 5); break;
+    case 256 * 16 + 6: CONVROT_RQ(256, 6); break;
+    case 256 * 16 + 7: CONVROT_RQ(256, 7); break;
+    case 256 * 16 + 8: CONVROT_RQ(256, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef CONVROT_RQ
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g, int8_t* codes,
+                               float* scale, hipStream_t stream) {
+  if (in_dtype == IN_BF16) return dispatch<IN_BF16, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
+  return dispatch<IN_F32, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
+}
+
+hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,
+                                     uint8_t* wq4, float* scale, int32_t* clip_index, hipStream_t stream) {
+  if (in_dtype == IN_BF16) return dispatch<IN_BF16, MODE_I4>(w, rows, K, log2g, wq4, scale, clip_index, stream);
+  return dispatch<IN_F32, MODE_I4>(w, rows, K, log2g, wq4, scale, clip_index, stream);
+}
+
+}  // namespace convrot
