@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Benchmark of the ConvRot W8A8 linear on one MI355X.
+
+Headline workload: one ConvRot W8A8 linear at the MLP up/gate shape
+M=2048 tokens, K=4096, N=12288, group 256 (bf16 activations N(0,1) with 1 %
+outlier channels x20, int8 per-row weights).  One step = one call of
+convrot_w8a8_linear (rotate + quantize the activations, int8 GEMM, bf16
+epilogue) with all inputs resident in HBM.  Steps cycle through several
+buffer sets whose total exceeds twice the 256 MB Infinity Cache, so every
+step reads its operands from HBM.
+
+Prints ONE JSON line on stdout: TOPS (2*M*N*K per step / step time), plus
+tokens/s, the GEMM kernel's roofline position (timed live with HIP events on
+the launch stream), the rotate-quantize kernel's HBM bandwidth, and the CPU
+oracle timed on a bounded sample on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--no-extras] [--profile {gemm,rq,copy,linear}]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, ops/s * 1e-12
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+MALL_BYTES = 256 << 20
+M, K, N, GROUP = 2048, 4096, 12288, 256
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMM_SOURCES = ["w8a8_quantized_linear_amd/csrc/gemm_i8.hip"]
+RQ_SOURCES = ["w8a8_quantized_linear_amd/csrc/rotate_quant.hip"]
+
+
+def load_traffic(name, sources):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(sources):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Timer:
+    """Average duration of repeated launches, from HIP events recorded on the
+    current stream (the one the library launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def time(self, fn, reps, warm=3):
+        torch = self.torch
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(reps):
+            fn(i)
+        e.record()
+        e.synchronize()
+        return s.elapsed_time(e) / 1e3 / reps  # seconds per launch
+
+
+def build_sets(torch, cr, wl, nsets):
+    x, w = wl.config_inputs("C3u")
+    dev = torch.device("cuda")
+    w_dev = torch.from_numpy(w).to(dev)
+    wq0, ws0 = cr.quantize_weight(w_dev, group=GROUP, bits=8)
+    del w_dev
+    x0 = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    sets = []
+    for i in range(nsets):
+        xi = x0.clone()
+        wqi = wq0.clone()
+        wsi = ws0.clone()
+        yi = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsp = cr.workspace(M, K, dev)
+        sets.append((xi, wqi, wsi, yi, wsp))
+    return x, w, sets
+
+
+def cpu_baseline(x, w, target_s=12.0):
+    """The CPU oracle as it stands, on the host cores: rotate+quantize a
+    sample of tokens, naive int32 GEMM against all N rows, bf16 epilogue.
+    Weight preparation is offline (not timed), as on the GPU side."""
+    import oracle
+    wq, ws = oracle.quantize_weight_i8(w, GROUP)
+    ms = 16
+    t0 = time.perf_counter()
+    oracle.w8a8_linear(np.ascontiguousarray(x[:ms]), wq, ws, GROUP)
+    t_probe = time.perf_counter() - t0
+    ms = int(min(M, max(16, ms * target_s / max(t_probe, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.w8a8_linear(np.ascontiguousarray(x[:ms]), wq, ws, GROUP)
+    t = time.perf_counter() - t0
+    return {
+        "value": 2.0 * ms * N * K / t / 1e12,
+        "unit": "TOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"first {ms} of {M} tokens, full K={K} x N={N} (GEMM cost is linear in tokens); "
+                  f"{t:.2f} s; weights quantized by the oracle beforehand (untimed)",
+        "tokens_per_s": ms / t,
+        "seconds": t,
+    }
+
+
+def check_parity(torch, cr, x, w, y_dev):
+    """Sampled parity of the benchmarked output against the oracle."""
+    import oracle
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(M, 16, replace=False))
+    rows = np.sort(rng.choice(N, 128, replace=False))
+    xq, xs = oracle.rotate_quant(np.ascontiguousarray(x[toks]), GROUP)
+    wq, ws = oracle.quantize_weight_i8(np.ascontiguousarray(w[rows]), GROUP)
+    y_ref = oracle.epilogue(oracle.gemm_i8(xq, wq), xs, ws)
+    y = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)[np.ix_(toks, rows)]
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return float(np.linalg.norm(f(y) - f(y_ref)) / np.linalg.norm(f(y_ref)))
+
+
+def extras_w4a8(torch, cr, wl, timer):
+    cfg = wl.CONFIGS["C5"]
+    lin = cfg.linears[0]
+    x, w = wl.config_inputs("C5")
+    dev = torch.device("cuda")
+    wq4, ws = cr.quantize_weight(torch.from_numpy(w).to(dev), bits=4)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty((cfg.M, lin.N), dtype=torch.bfloat16, device=dev)
+    wsp = cr.workspace(cfg.M, lin.K, dev)
+    t = timer.time(lambda i: cr.w4a8_linear(xd, wq4, ws, out=y, ws=wsp), 50)
+    ops = 2.0 * cfg.M * lin.N * lin.K
+    return {"workload": "W4A8 M=4096 K=4096 N=12288", "tops": ops / t / 1e12, "us": t * 1e6,
+            "tokens_per_s": cfg.M / t, "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
+
+
+def extras_stack(torch, cr, wl, timer):
+    """32-layer synthetic decoder linear stack at M=8704: 224 linear calls per
+    pass (each with its own rotate-quantize), weights generated on device."""
+    cfg = wl.CONFIGS["C4"]
+    dev = torch.device("cuda")
+    acts = [torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16) for a in wl.stack_activations()]
+    layers = []
+    for layer in range(cfg.layers):
+        ws_ = []
+        for li, lin in enumerate(cfg.linears):
+            wd = wl.make_weight_device(lin.N, lin.K, wl.C4_WEIGHT_SEED_BASE + layer * 16 + li, dev)
+            ws_.append(cr.quantize_weight(wd))
+            del wd
+        layers.append(ws_)
+    outs = {n: torch.empty((cfg.M, n), dtype=torch.bfloat16, device=dev) for n in {l.N for l in cfg.linears}}
+    wsp = cr.workspace(cfg.M, 12288, dev)
+    ops = 0.0
+    for lin in cfg.linears:
+        ops += 2.0 * cfg.M * lin.N * lin.K
+    ops *= cfg.layers
+
+    def one_pass(_):
+        for layer in range(cfg.layers):
+            for li, lin in enumerate(cfg.linears):
+                wq, wsc = layers[layer][li]
+                cr.w8a8_linear(acts[wl.C4_INPUT_OF[lin.name]], wq, wsc, out=outs[lin.N], ws=wsp)
+
+    t = timer.time(one_pass, 3, warm=1)
+    return {"workload": "32-layer linear stack, M=8704 (34 x 256 tokens), 224 W8A8 linears",
+            "ms_per_pass": t * 1e3, "tokens_per_s": cfg.M / t, "tops": ops / t / 1e12,
+            "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
+
+
+def profile_mode(mode, torch, cr, wl):
+    """Short runs for rocprofv3 counter collection (a handful of launches)."""
+    dev = torch.device("cuda")
+    if mode == "copy":
+        n = 1 << 30
+        a = torch.empty((n,), dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n} bytes")
+        return
+    x, w, sets = build_sets(torch, cr, wl, 1)
+    xd, wq, ws, y, wsp = sets[0]
+    xq, xs = cr.rotate_quant(xd)
+    for _ in range(3):
+        if mode == "gemm":
+            cr.convrot_gemm_i8(xq, xs, wq, 8, ws, M, N, K, None, y)
+        elif mode == "rq":
+            cr.convrot_rotate_quant(xd, M, K, GROUP, xq, xs)
+        else:
+            cr.w8a8_linear(xd, wq, ws, out=y, ws=wsp)
+    torch.cuda.synchronize()
+    log(f"profile mode {mode}: 3 launches")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--profile", choices=["gemm", "rq", "copy", "linear"], default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the ConvRot linear runs on a single MI355X); "
+              "multi-GPU runs are not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import w8a8_quantized_linear_amd as cr
+    from w8a8_quantized_linear_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    cr.load()
+
+    if args.profile:
+        profile_mode(args.profile, torch, cr, wl)
+        return
+
+    per_set = M * K * 2 + N * K + N * 4 + M * N * 2 + cr.convrot_workspace_size(M, K)
+    nsets = max(2, -(-2 * MALL_BYTES // per_set) + 1)
+    log(f"building {nsets} buffer sets of {per_set / 2**20:.1f} MiB")
+    x, w, sets = build_sets(torch, cr, wl, nsets)
+    timer = Timer(torch)
+
+    def step(i):
+        xd, wq, ws, y, wsp = sets[i % nsets]
+        cr.w8a8_linear(xd, wq, ws, group=GROUP, out=y, ws=wsp)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_step = start.elapsed_time(end) / 1e3 / args.steps
+    log(f"timed {args.steps} steps: {t_step * 1e6:.1f} us/step (host wall {wall * 1e3:.1f} ms)")
+
+    ops = 2.0 * M * N * K
+    tops = ops / t_step / 1e12
+
+    # Per-kernel durations, live, on the launch stream.
+    q = [cr.rotate_quant(s[0]) for s in sets]
+    t_gemm = timer.time(lambda i: cr.convrot_gemm_i8(q[i % nsets][0], q[i % nsets][1], sets[i % nsets][1], 8,
+                                                     sets[i % nsets][2], M, N, K, None, sets[i % nsets][3]),
+                        max(50, args.steps))
+    t_rq = timer.time(lambda i: cr.convrot_rotate_quant(sets[i % nsets][0], M, K, GROUP, q[i % nsets][0],
+                                                        q[i % nsets][1]), max(50, args.steps))
+    # resident (hot) variant of the whole step, for reference
+    t_hot = timer.time(lambda i: cr.w8a8_linear(sets[0][0], sets[0][1], sets[0][2], out=sets[0][3],
+                                                ws=sets[0][4]), max(50, args.steps))
+    gemm_tops = ops / t_gemm / 1e12
+    rq_bytes = M * (3 * K + 4)
+    rq_gbs = rq_bytes / t_rq / 1e9
+
+    rel = check_parity(torch, cr, x, w, sets[(args.steps - 1) % nsets][3])
+    log(f"parity (sampled, vs oracle): rel L2 {rel:.2e}")
+
+    out = {
+        "metric": "W8A8 ConvRot linear TOPS & tokens/s (M=2048,K=4096,N=12288); % int8 MFMA peak",
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "ConvRot W8A8 linear, MLP up/gate shape: M=2048 tokens, K=4096, N=12288, "
+                               "group 256, bf16 N(0,1) activations with 1% outlier channels x20, int8 per-row "
+                               "weights; operands cycled through buffer sets larger than 2x the MALL",
+                   "M": M, "K": K, "N": N, "group": GROUP, "buffer_sets": nsets},
+        "tokens_per_s": round(M / t_step, 1),
+        "pct_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
+        "hot_tops": round(ops / t_hot / 1e12, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_i8_kernel (int8 MFMA GEMM + bf16 epilogue)",
+            "achieved": round(gemm_tops, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOPS",
+            "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": load_traffic("gemm_i8_C3u", GEMM_SOURCES),
+            "avg_launch_us": round(t_gemm * 1e6, 3),
+            "algorithmic_ops_per_launch": ops,
+        },
+        "rotate_quant": {
+            "bound": "hbm",
+            "achieved": round(rq_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(rq_gbs / PEAK_HBM_GBS, 4),
+            "avg_launch_us": round(t_rq * 1e6, 3),
+            "algorithmic_bytes_per_launch": rq_bytes,
+            "traffic": load_traffic("rotate_quant_C3u", RQ_SOURCES),
+        },
+        "parity_rel_l2_sampled": rel,
+    }
+    if not args.no_extras:
+        log("extras: W4A8 M=4096 K=4096 N=12288")
+        out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
+        log("extras: 32-layer stack M=8704")
+        out["stack"] = extras_stack(torch, cr, wl, timer)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on the host cores")
+        out["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
