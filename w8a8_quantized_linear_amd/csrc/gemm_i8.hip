@@ -7,213 +7,469 @@
 //   acc[m][n] = sum_k xq[m][k] * wq[n][k]           (both operands K-major)
 //   y[m][n]   = bf16_rne(((float)acc * x_scale[m]) * w_scale[n])
 //
-// Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN output
-// tile; each wave owns a (BM/2) x (BN/2) sub-tile made of 32x32 blocks, each
-// accumulated by v_mfma_i32_32x32x32_i8.  K advances in steps of BK = 128
-// bytes through two LDS buffers (load of step s+1 overlaps the MFMAs of step
-// s; one barrier per step).  LDS rows are 128 bytes; 16-byte chunk c of row r
-// is stored at chunk c ^ h(r), h(r) = (r & 7) ^ ((r >> 3) & 1), so that the
-// 16-byte operand reads of 8 or 16 consecutive rows hit distinct banks.
+// Tiling.  A 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN output
+// tile (BM tokens x BN weight rows); each wave owns a (BM/2) x (BN/2)
+// sub-tile of 32x32 blocks accumulated by v_mfma_i32_32x32x32_i8.  The MFMA's
+// first operand is the weight tile and its second the token tile, so a lane's
+// 16 accumulators of a block cover one token and four runs of four
+// consecutive weight rows: the epilogue writes 8-byte bf16 runs.
 //
-// int4 weights are unpacked while being staged into LDS: a nibble q becomes
-// the byte 16*q (a mask, no shifts), so the accumulator holds 16*acc exactly
-// and is shifted back by 4 before the epilogue.
+// Pipeline.  K advances 64 at a time through a ring of 4 LDS stages filled
+// by buffer_load_dwordx4 ... lds (global -> LDS without registers; each wave
+// instruction moves a 1 KB block).  Rows past M / N and the K tail read as
+// zero through the buffer descriptor's range check.  A step has two phases
+// split by one workgroup barrier:
+//   phase 1: slice-0 MFMAs (K 0..31 of the step), interleaved with the
+//            LDS reads of slice 1 and the token-tile loads of stage kt+3;
+//   wait until stage kt+1 has landed (vmcnt), barrier;
+//   phase 2: slice-1 MFMAs, interleaved with the weight-tile loads of
+//            stage kt+4 (into the buffer just consumed) and the LDS reads of
+//            the next step's slice 0.
+// Loads and LDS reads are spread one per MFMA: the load path moves about
+// 64 B/clk per CU and a wave stalled behind a burst of loads would let the
+// matrix pipe drain within one MFMA.  The step count is padded to a multiple
+// of 4 and the body has no conditionals (steps past the end of K read zeros),
+// so the compiler's count of outstanding loads stays exact.
+//
+// LDS rows are 64 bytes (4 chunks of 16 B); chunk c of row r is stored at
+// chunk c ^ h(r), h(r) = ((r >> 2) ^ (r >> 3)) & 3.  Packed int4 weight rows
+// are 32 bytes (2 chunks), swizzled by ((r >> 2) ^ (r >> 3)) & 1.  Both were
+// chosen by measuring ds_read_b128 throughput for these exact fragment
+// access patterns on gfx950 (about 240 B/clk per CU, against about 140 for
+// swizzles that leave two-way bank conflicts).
+//
+// int4 weights: a lane reads the 16 packed bytes covering both 32-wide K
+// slices of the step and unpacks them in registers; a nibble q becomes the
+// byte 16*q (masks and byte permutes), so the accumulator holds 16*acc exactly
+// and is shifted back by 4 before the epilogue.  For this the K order inside
+// a step is permuted identically for both operands (lane half h, slice s
+// takes k = 32h + 16s .. +16), which leaves the dot products unchanged.
+//
+// Tiles are assigned so that each of the 8 XCDs (workgroups are dispatched to
+// them round-robin) works on a contiguous block of tiles that share weight
+// and token rows in its L2.
 #include "convrot_internal.h"
+
+#include <cstdio>
+#include <cstdlib>
 
 namespace convrot {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
-constexpr int BK = 128;
+constexpr int kStages = 4;
+constexpr int BK = 64;
+constexpr unsigned kOOB = 0x7ffffff0u;  // buffer offset beyond every range: reads as zero
+constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz64(int r) { return ((r >> 2) ^ (r >> 3)) & 3; }
+__device__ __forceinline__ int swz32(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  return u >> 16;
 }
 
-// 16 packed bytes (32 nibbles, k = 0..31) -> two 16-byte chunks of 16*q bytes
-// in natural k order.
-__device__ __forceinline__ void unpack_nibbles(uint4 p, uint4& c0, uint4& c1) {
-  uint32_t w[4] = {p.x, p.y, p.z, p.w};
-  uint32_t o[8];
+// 4 packed bytes (8 nibbles, k = 0..7) -> 8 bytes of 16*q in natural k order.
+__device__ __forceinline__ void unpack4(uint32_t w, uint32_t& o0, uint32_t& o1) {
+  const uint32_t lo = (w << 4) & 0xf0f0f0f0u;  // even k, times 16
+  const uint32_t hi = w & 0xf0f0f0f0u;          // odd k, times 16
+  o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
+}
+
+// Scheduling pattern for one phase: NM MFMAs, each followed by one
+// instruction of class A (NA of them), then of class B (NB of them), until
+// all are placed; a full scheduling barrier closes the phase.  Masks: 0x008
+// MFMA, 0x020 VMEM read, 0x100 DS read.
+template <int NM, int NA, int MA, int NB, int MB>
+__device__ __forceinline__ void interleave_phase() {
+  constexpr int N_MEM = NA + NB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t lo = (w[i] << 4) & 0xf0f0f0f0u;  // even k, times 16
-    uint32_t hi = w[i] & 0xf0f0f0f0u;          // odd k, times 16
-    o[2 * i] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-    o[2 * i + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+  for (int i = 0; i < (NM > N_MEM ? NM : N_MEM); ++i) {
+    if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NA) __builtin_amdgcn_sched_group_barrier(MA, 1, 0);
+    else if (i - NA < NB) __builtin_amdgcn_sched_group_barrier(MB, 1, 0);
   }
-  c0 = make_uint4(o[0], o[1], o[2], o[3]);
-  c1 = make_uint4(o[4], o[5], o[6], o[7]);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int BM, int BN, bool W4>
-__global__ __launch_bounds__(kThreads) void gemm_i8_kernel(const int8_t* __restrict__ A,
-                                                           const float* __restrict__ sa,
-                                                           const uint8_t* __restrict__ B,
-                                                           const float* __restrict__ sb, int M, int N, int K,
-                                                           int tiles_n, int32_t* __restrict__ acc_out,
-                                                           uint16_t* __restrict__ y) {
-  constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
-  constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int A_CHUNKS = BM * BK / 16;
-  constexpr int B_CHUNKS = BN * BK / 16;
-  constexpr int A_PER_T = A_CHUNKS / kThreads;
-  constexpr int B_PER_T = W4 ? (BN * BK / 32) / kThreads : B_CHUNKS / kThreads;
-  static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small for the thread count");
+struct Cfg {
+  static constexpr int WM = BM / 2, WN = BN / 2;    // wave extent: tokens, weight rows
+  static constexpr int TI = WN / 32, TJ = WM / 32;  // 32x32 blocks along n and m
+  static constexpr int WROW = W4 ? 32 : 64;         // weight bytes per row per stage
+  static constexpr int W_BYTES = BN * WROW;
+  static constexpr int X_BYTES = BM * 64;
+  static constexpr int W_LOADS = W_BYTES / 4096;    // 1 KB per wave instruction, 4 waves
+  static constexpr int X_LOADS = X_BYTES / 4096;
+  static constexpr int LOADS = W_LOADS + X_LOADS;   // per wave per stage
+  static_assert(W_LOADS * 4096 == W_BYTES && X_LOADS * 4096 == X_BYTES, "tile must split into 4 KB");
+  static_assert(3 * LOADS < 64, "vmcnt budget");
+};
 
-  __shared__ __attribute__((aligned(16))) int8_t lds[2][(BM + BN) * BK];
+template <int BM, int BN, bool W4>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __restrict__ X,
+                                                              const float* __restrict__ sx,
+                                                              const uint8_t* __restrict__ W,
+                                                              const float* __restrict__ sw, int M, int N, int K,
+                                                              int tiles_m, int tiles_n,
+                                                              int32_t* __restrict__ acc_out,
+                                                              uint16_t* __restrict__ y) {
+  using C = Cfg<BM, BN, W4>;
+  constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS;
+  __shared__ __attribute__((aligned(1024))) int8_t sW0[C::W_BYTES], sW1[C::W_BYTES], sW2[C::W_BYTES],
+      sW3[C::W_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sX0[C::X_BYTES], sX1[C::X_BYTES], sX2[C::X_BYTES],
+      sX3[C::X_BYTES];
+  int8_t* const sWs[kStages] = {sW0, sW1, sW2, sW3};
+  int8_t* const sXs[kStages] = {sX0, sX1, sX2, sX3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int tile_m = blockIdx.x / tiles_n;
-  const int tile_n = blockIdx.x % tiles_n;
+  const int row = lane & 31, half = lane >> 5;
+
+  // XCD-aware tile order: block b runs on XCD b % 8; XCD x takes the x-th
+  // contiguous slice of tiles (token tiles vary fastest).
+  const int T = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int tile_m = t % tiles_m, tile_n = t / tiles_m;
   const int m0 = tile_m * BM, n0 = tile_n * BN;
-  const int64_t Kb = W4 ? K / 2 : K;  // bytes per weight row
+  const int Kb = W4 ? K / 2 : K;  // bytes per weight row
 
-  uint4 ra[A_PER_T];
-  uint4 rb[B_PER_T];
+  // Buffer descriptors over this tile's rows only; rows past M / N fall
+  // outside num_records and read as zero.
+  const int rows_x = min(BM, M - m0), rows_w = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(X + int64_t(m0) * K), short(0), rows_x * K, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(W + int64_t(n0) * Kb), short(0), rows_w * Kb, kBufFlags);
 
-  auto load_global = [&](int k0) {
+  // Per-lane byte offsets (at k0 = 0) of this wave's load blocks, and the k
+  // each lane's chunk starts at.  Lane i's chunk lands at byte 16 i of the
+  // block, so the swizzle is applied through the choice of source chunk.
+  unsigned offw[C::W_LOADS], offx[C::X_LOADS];
+  int kw[C::W_LOADS], kx[C::X_LOADS];
 #pragma unroll
-    for (int j = 0; j < A_PER_T; ++j) {
-      const int id = tid + j * kThreads;
-      const int r = id / (BK / 16), c = id % (BK / 16);
-      const int gm = m0 + r, gk = k0 + c * 16;
-      ra[j] = (gm < M && gk < K) ? *reinterpret_cast<const uint4*>(A + int64_t(gm) * K + gk)
-                                 : make_uint4(0, 0, 0, 0);
+  for (int j = 0; j < C::W_LOADS; ++j) {
+    const int b = wave * C::W_LOADS + j;
+    if constexpr (W4) {
+      const int r = b * 32 + (lane >> 1);
+      const int h = (lane & 1) ^ swz32(r);
+      kw[j] = 32 * h;
+      offw[j] = unsigned(r * Kb + 16 * h);
+    } else {
+      const int r = b * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz64(r);
+      kw[j] = 16 * c;
+      offw[j] = unsigned(r * Kb + 16 * c);
     }
+  }
 #pragma unroll
-    for (int j = 0; j < B_PER_T; ++j) {
-      const int id = tid + j * kThreads;
-      if constexpr (W4) {
-        const int r = id / (BK / 32), pc = id % (BK / 32);
-        const int gn = n0 + r, gk = k0 + pc * 32;
-        rb[j] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(B + int64_t(gn) * Kb + gk / 2)
-                                   : make_uint4(0, 0, 0, 0);
-      } else {
-        const int r = id / (BK / 16), c = id % (BK / 16);
-        const int gn = n0 + r, gk = k0 + c * 16;
-        rb[j] = (gn < N && gk < K) ? *reinterpret_cast<const uint4*>(B + int64_t(gn) * Kb + gk)
-                                   : make_uint4(0, 0, 0, 0);
-      }
+  for (int j = 0; j < C::X_LOADS; ++j) {
+    const int b = wave * C::X_LOADS + j;
+    const int r = b * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ swz64(r);
+    kx[j] = 16 * c;
+    offx[j] = unsigned(r * K + 16 * c);
+  }
+
+  auto issue_w = [&](int s, int k0) {
+    const unsigned kw_bytes = W4 ? unsigned(k0 / 2) : unsigned(k0);
+#pragma unroll
+    for (int j = 0; j < C::W_LOADS; ++j) {
+      const unsigned off = (k0 + kw[j] < K) ? offw[j] + kw_bytes : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sWs[s] + (wave * C::W_LOADS + j) * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  auto issue_x = [&](int s, int k0) {
+#pragma unroll
+    for (int j = 0; j < C::X_LOADS; ++j) {
+      const unsigned off = (k0 + kx[j] < K) ? offx[j] + unsigned(k0) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_ptr_t)(sXs[s] + (wave * C::X_LOADS + j) * 1024), 16,
+                                               off, 0, 0, 0);
     }
   };
 
-  auto store_lds = [&](int buf) {
-    int8_t* sA = lds[buf];
-    int8_t* sB = lds[buf] + BM * BK;
+  // Fragment row offsets inside a stage (constant over K).
+  int wrow_off[TI], xrow_off[TJ], wsw[TI], xsw[TJ];
 #pragma unroll
-    for (int j = 0; j < A_PER_T; ++j) {
-      const int id = tid + j * kThreads;
-      const int r = id / (BK / 16), c = id % (BK / 16);
-      *reinterpret_cast<uint4*>(sA + r * BK + 16 * (c ^ swz(r))) = ra[j];
-    }
+  for (int i = 0; i < TI; ++i) {
+    const int r = wn * WN + i * 32 + row;
+    wrow_off[i] = r * C::WROW;
+    wsw[i] = W4 ? swz32(r) : swz64(r);
+  }
 #pragma unroll
-    for (int j = 0; j < B_PER_T; ++j) {
-      const int id = tid + j * kThreads;
-      if constexpr (W4) {
-        const int r = id / (BK / 32), pc = id % (BK / 32);
-        uint4 c0, c1;
-        unpack_nibbles(rb[j], c0, c1);
-        *reinterpret_cast<uint4*>(sB + r * BK + 16 * ((2 * pc) ^ swz(r))) = c0;
-        *reinterpret_cast<uint4*>(sB + r * BK + 16 * ((2 * pc + 1) ^ swz(r))) = c1;
+  for (int j = 0; j < TJ; ++j) {
+    const int r = wm * WM + j * 32 + row;
+    xrow_off[j] = r * 64;
+    xsw[j] = swz64(r);
+  }
+
+  // fa[s][i]: weight fragments for K-slice s; fb[s][j]: token fragments.
+  v4i fa[2][TI], fb[2][TJ];
+  uint2 pw_hi[TI];  // int4 weights: packed bytes of slice 1, unpacked late
+
+  auto read_x = [&](int s, int slice) {
+    const int8_t* sX = sXs[s];
+    const int c = W4 ? 2 * half + slice : 2 * slice + half;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+      fb[slice][j] = *reinterpret_cast<const v4i*>(sX + xrow_off[j] + 16 * (c ^ xsw[j]));
+  };
+  // W8: one 16-byte read per fragment and slice.  W4: the slice-0 read
+  // fetches the 16 packed bytes of both slices, unpacks slice 0 and keeps the
+  // packed slice-1 half until the slice-1 call unpacks it (the current
+  // step's slice-1 fragments are still in use when the next step's slice 0
+  // is read).
+  auto read_w = [&](int s, int slice) {
+    const int8_t* sW = sWs[s];
+    if constexpr (W4) {
+      if (slice == 0) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          const uint4 p = *reinterpret_cast<const uint4*>(sW + wrow_off[i] + 16 * (half ^ wsw[i]));
+          uint32_t o[4];
+          unpack4(p.x, o[0], o[1]);
+          unpack4(p.y, o[2], o[3]);
+          fa[0][i] = v4i{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+          pw_hi[i] = make_uint2(p.z, p.w);
+        }
       } else {
-        const int r = id / (BK / 16), c = id % (BK / 16);
-        *reinterpret_cast<uint4*>(sB + r * BK + 16 * (c ^ swz(r))) = rb[j];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          uint32_t o[4];
+          unpack4(pw_hi[i].x, o[0], o[1]);
+          unpack4(pw_hi[i].y, o[2], o[3]);
+          fa[1][i] = v4i{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+        }
       }
+    } else {
+      const int c = 2 * slice + half;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+        fa[slice][i] = *reinterpret_cast<const v4i*>(sW + wrow_off[i] + 16 * (c ^ wsw[i]));
     }
   };
 
-  v16i acc[TM][TN];
+  v16i acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  const int ktiles = (K + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
+  auto mfma_slice = [&](int slice) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[slice][i], fb[slice][j], acc[i][j], 0, 0, 0);
+  };
 
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ktiles) load_global((kt + 1) * BK);
-    const int8_t* sA = lds[buf];
-    const int8_t* sB = lds[buf] + BM * BK;
+  // Barrier between the phases.  This wave's LDS reads of the consumed
+  // stage must be complete (lgkmcnt 0) before other waves refill it; the
+  // asynchronous LDS writes are covered by the explicit vmcnt wait that
+  // precedes this call.  The empty asm statements keep the compiler from
+  // moving LDS accesses across.
+  auto sync_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // LDS reads per phase, for the interleaving pattern.
+  constexpr int R1 = (W4 ? 0 : TI) + TJ;  // phase 1: slice-1 reads
+  constexpr int R2 = TI + TJ;             // phase 2: next slice-0 reads
+
+  const int ksteps = ((K + BK - 1) / BK + kStages - 1) / kStages * kStages;
+
+  // Prologue: stages 0..2 and the weight half of stage 3 are issued; stage 0
+  // has landed once at most 2 L + W_LOADS newer loads are outstanding.
+  issue_w(0, 0);
+  issue_x(0, 0);
+  issue_w(1, BK);
+  issue_x(1, BK);
+  issue_w(2, 2 * BK);
+  issue_x(2, 2 * BK);
+  issue_w(3, 3 * BK);
+  wait_vmcnt<2 * L + C::W_LOADS>();
+  sync_stage();
+  read_w(0, 0);
+  read_x(0, 0);
+
+  // Step kt issues the token loads of stage kt+3 in phase 1 and the weight
+  // loads of stage kt+4 in phase 2.  Before the barrier of step kt, stage
+  // kt+1 must be complete; the loads issued after its last one are those of
+  // stages kt+2 and kt+3, i.e. 2 L.
+  for (int kb = 0; kb < ksteps; kb += kStages) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 32; ++kk) {
-      const int c = 2 * kk + (lane >> 5);
-      v4i a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = wm * WM + i * 32 + (lane & 31);
-        a[i] = *reinterpret_cast<const v4i*>(sA + r * BK + 16 * (c ^ swz(r)));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int r = wn * WN + j * 32 + (lane & 31);
-        b[j] = *reinterpret_cast<const v4i*>(sB + r * BK + 16 * (c ^ swz(r)));
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+    for (int s = 0; s < kStages; ++s) {
+      const int kt = kb + s;
+      read_w(s, 1);
+      read_x(s, 1);
+      mfma_slice(0);
+      issue_x((s + 3) % kStages, (kt + 3) * BK);
+      interleave_phase<TI * TJ, R1, 0x100, C::X_LOADS, 0x020>();
+      wait_vmcnt<2 * L>();
+      sync_stage();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(s, (kt + 4) * BK);
+      read_w((s + 1) % kStages, 0);
+      read_x((s + 1) % kStages, 0);
+      mfma_slice(1);
+      interleave_phase<TI * TJ, C::W_LOADS, 0x020, R2, 0x100>();
     }
-    if (kt + 1 < ktiles) store_lds(buf ^ 1);
-    __syncthreads();
   }
+  wait_vmcnt<0>();
 
-  // Epilogue.  32x32 block layout: lane holds column (lane & 31) and rows
-  // 8*(e/4) + 4*(lane/32) + (e%4) for e = 0..15.
+  // Epilogue.  Block (i, j): lane holds token m = ... + (lane & 31) and weight
+  // rows n = ... + 8*g + 4*(lane >> 5) + (0..3) in accumulators 4g..4g+3.
+  // All scales this lane needs are fetched in one batch first, so their
+  // latency is paid once rather than per output group.
+  const bool vec_ok = (N & 3) == 0;
+  float swv[TI][4][4];
+  float sxv[TJ];
+  if (y) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * WN + j * 32 + (lane & 31);
-      const float swn = (y && n < N) ? sb[n] : 0.f;
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * WM + i * 32 + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-        if (m < M && n < N) {
-          int a = acc[i][j][e];
-          if constexpr (W4) a >>= 4;
-          if (acc_out) acc_out[int64_t(m) * N + n] = a;
-          if (y) y[int64_t(m) * N + n] = f32_to_bf16_rne((float(a) * sa[m]) * swn);
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half + e;
+          swv[i][g][e] = n < N ? sw[n] : 0.f;
+        }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + j * 32 + row;
+      sxv[j] = m < M ? sx[m] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int m = m0 + wm * WM + j * 32 + row;
+    if (m >= M) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
+        int a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a[e] = acc[i][j][4 * g + e];
+          if constexpr (W4) a[e] >>= 4;
+        }
+        if (vec_ok && n + 3 < N) {
+          if (acc_out) *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = make_int4(a[0], a[1], a[2], a[3]);
+          if (y) {
+            uint32_t b[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne((float(a[e]) * sxv[j]) * swv[i][g][e]);
+            *reinterpret_cast<uint2*>(y + int64_t(m) * N + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e < N) {
+              if (acc_out) acc_out[int64_t(m) * N + n + e] = a[e];
+              if (y) y[int64_t(m) * N + n + e] = uint16_t(f32_to_bf16_rne((float(a[e]) * sxv[j]) * swv[i][g][e]));
+            }
+          }
         }
       }
     }
   }
 }
 
+template <int BM, int BN, bool W4>
+hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M,
+                      int N, int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  const dim3 grid(unsigned(tiles_m) * unsigned(tiles_n));
+  hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, W4>), grid, dim3(kThreads), 0, stream, xq, x_scale, wq, w_scale, M,
+                     N, K, tiles_m, tiles_n, acc_out, y);
+  return hipGetLastError();
+}
+
+struct TileChoice {
+  int bm, bn;
+};
+
+// Pick the macro tile: fewest rounds of tiles over the 256 CUs, weighted by
+// how efficiently each tile size runs (larger tiles reuse LDS operands more).
+TileChoice choose_tile(int64_t M, int64_t N, bool w4) {
+  static const TileChoice cands[] = {{256, 256}, {256, 192}, {256, 128}, {128, 256}, {128, 128}};
+  static const double eff[] = {1.0, 0.97, 0.85, 0.85, 0.6};
+  const int cus = 256;
+  double best = 1e300;
+  TileChoice pick = cands[4];
+  for (int c = 0; c < 5; ++c) {
+    if (w4 && cands[c].bn == 192) continue;  // packed weight tile must split into 4 KB loads
+    const int64_t tiles = ((M + cands[c].bm - 1) / cands[c].bm) * ((N + cands[c].bn - 1) / cands[c].bn);
+    const int64_t rounds = (tiles + cus - 1) / cus;
+    const double cost = double(rounds) * cands[c].bm * cands[c].bn / eff[c];
+    if (cost < best * 0.999) {
+      best = cost;
+      pick = cands[c];
+    }
+  }
+  return pick;
+}
+
+// CONVROT_GEMM_TILE=<BM>x<BN> forces one of the tile shapes above (a tuning
+// override for sweeps; every tile gives bit-identical results).
+TileChoice tile_override() {
+  static const TileChoice forced = [] {
+    TileChoice t{0, 0};
+    if (const char* s = getenv("CONVROT_GEMM_TILE")) {
+      if (sscanf(s, "%dx%d", &t.bm, &t.bn) != 2) t = {0, 0};
+    }
+    return t;
+  }();
+  return forced;
+}
+
+template <bool W4>
+hipError_t launch_w(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M, int N,
+                    int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  TileChoice tc = tile_override();
+  if (tc.bm == 0 || (W4 && tc.bn == 192)) tc = choose_tile(M, N, W4);
+  if (tc.bm == 256 && tc.bn == 256) return launch_cfg<256, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  if constexpr (!W4)
+    if (tc.bm == 256 && tc.bn == 192) return launch_cfg<256, 192, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_cfg<256, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  if (tc.bm == 128 && tc.bn == 256) return launch_cfg<128, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  return launch_cfg<128, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
-  const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = int((N + BN - 1) / BN);
-  const dim3 grid(unsigned(tiles_m) * unsigned(tiles_n));
-  const uint8_t* B = static_cast<const uint8_t*>(wq);
-  if (wbits == 4) {
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, true>), grid, dim3(kThreads), 0, stream, xq, x_scale, B, w_scale,
-                       int(M), int(N), int(K), tiles_n, acc_out, y);
-  } else {
-    hipLaunchKernelGGL((gemm_i8_kernel<BM, BN, false>), grid, dim3(kThreads), 0, stream, xq, x_scale, B, w_scale,
-                       int(M), int(N), int(K), tiles_n, acc_out, y);
-  }
-  return hipGetLastError();
+  const uint8_t* W = static_cast<const uint8_t*>(wq);
+  if (wbits == 4) return launch_w<true>(xq, x_scale, W, w_scale, int(M), int(N), int(K), acc_out, y, stream);
+  return launch_w<false>(xq, x_scale, W, w_scale, int(M), int(N), int(K), acc_out, y, stream);
 }
 
 }  // namespace convrot
