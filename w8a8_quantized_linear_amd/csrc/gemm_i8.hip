@@ -12,7 +12,8 @@
 // sub-tile of 32x32 blocks accumulated by v_mfma_i32_32x32x32_i8.  The MFMA's
 // first operand is the weight tile and its second the token tile, so a lane's
 // 16 accumulators of a block cover one token and four runs of four
-// consecutive weight rows: the epilogue writes 8-byte bf16 runs.
+// consecutive weight rows; the epilogue regroups them through LDS into
+// 16-byte row-contiguous bf16 stores.
 //
 // Pipeline.  K advances 64 at a time through a ring of 4 LDS stages filled
 // by buffer_load_dwordx4 ... lds (global -> LDS without registers; each wave
@@ -69,10 +70,12 @@ constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 fa
 __device__ __forceinline__ int swz64(int r) { return ((r >> 2) ^ (r >> 3)) & 3; }
 __device__ __forceinline__ int swz32(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // 4 packed bytes (8 nibbles, k = 0..7) -> 8 bytes of 16*q in natural k order.
@@ -90,19 +93,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xf) | (0x7 << 4) | (0xf << 8) | ((N >> 4) << 14));
 }
 
-// Scheduling pattern for one phase: NM MFMAs, each followed by one
-// instruction of class A (NA of them), then of class B (NB of them), until
-// all are placed; a full scheduling barrier closes the phase.  Masks: 0x008
-// MFMA, 0x020 VMEM read, 0x100 DS read.
-template <int NM, int NA, int MA, int NB, int MB>
+// Scheduling pattern for one phase: NM MFMAs; the ND LDS reads go one per
+// MFMA from the start of the phase (so they have completed by the wait that
+// ends it), the NV buffer loads are spread evenly over the whole phase (so
+// the load path never sees a burst); a full scheduling barrier closes it.
+template <int NM, int NV, int ND>
 __device__ __forceinline__ void interleave_phase() {
-  constexpr int N_MEM = NA + NB;
+  int nv = 0;
 #pragma unroll
-  for (int i = 0; i < (NM > N_MEM ? NM : N_MEM); ++i) {
-    if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NA) __builtin_amdgcn_sched_group_barrier(MA, 1, 0);
-    else if (i - NA < NB) __builtin_amdgcn_sched_group_barrier(MB, 1, 0);
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < ND) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    const int v_due = ((i + 1) * NV) / NM;  // loads due after MFMA i
+    if (nv < v_due) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      ++nv;
+    }
   }
+  for (int i = NM; i < ND; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  for (; nv < NV; ++nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __re
       read_x(s, 1);
       mfma_slice(0);
       issue_x((s + 3) % kStages, (kt + 3) * BK);
-      interleave_phase<TI * TJ, R1, 0x100, C::X_LOADS, 0x020>();
+      interleave_phase<TI * TJ, C::X_LOADS, R1>();
       wait_vmcnt<2 * L>();
       sync_stage();
       __builtin_amdgcn_sched_barrier(0);
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __re
       read_w((s + 1) % kStages, 0);
       read_x((s + 1) % kStages, 0);
       mfma_slice(1);
-      interleave_phase<TI * TJ, C::W_LOADS, 0x020, R2, 0x100>();
+      interleave_phase<TI * TJ, C::W_LOADS, R2>();
     }
   }
   wait_vmcnt<0>();
@@ -344,8 +353,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __re
   // Epilogue.  Block (i, j): lane holds token m = ... + (lane & 31) and weight
   // rows n = ... + 8*g + 4*(lane >> 5) + (0..3) in accumulators 4g..4g+3.
   // All scales this lane needs are fetched in one batch first, so their
-  // latency is paid once rather than per output group.
-  const bool vec_ok = (N & 3) == 0;
+  // latency is paid once.  The bf16 results of one 32-token block at a time
+  // are staged in LDS (wave w uses token stage buffer w, free once every
+  // wave has left the main loop) and leave as 16-byte row-contiguous stores;
+  // writing straight from the accumulator layout would scatter 8-byte pieces
+  // over 32 rows per instruction.
   float swv[TI][4][4];
   float sxv[TJ];
   if (y) {
@@ -364,40 +376,90 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __re
       sxv[j] = m < M ? sx[m] : 0.f;
     }
   }
+  if (acc_out) {
+    const bool vec_ok = (N & 3) == 0;
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int m = m0 + wm * WM + j * 32 + row;
-    if (m >= M) continue;
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + j * 32 + row;
+      if (m >= M) continue;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
-        int a[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = acc[i][j][4 * g + e];
-          if constexpr (W4) a[e] >>= 4;
-        }
-        if (vec_ok && n + 3 < N) {
-          if (acc_out) *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = make_int4(a[0], a[1], a[2], a[3]);
-          if (y) {
-            uint32_t b[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) b[e] = f32_to_bf16_rne((float(a[e]) * sxv[j]) * swv[i][g][e]);
-            *reinterpret_cast<uint2*>(y + int64_t(m) * N + n) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
-          }
-        } else {
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
+          int a[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (n + e < N) {
-              if (acc_out) acc_out[int64_t(m) * N + n + e] = a[e];
-              if (y) y[int64_t(m) * N + n + e] = uint16_t(f32_to_bf16_rne((float(a[e]) * sxv[j]) * swv[i][g][e]));
-            }
+            a[e] = acc[i][j][4 * g + e];
+            if constexpr (W4) a[e] >>= 4;
           }
+          if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = make_int4(a[0], a[1], a[2], a[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) acc_out[int64_t(m) * N + n + e] = a[e];
+          }
+        }
+    }
+  }
+  if (!y) return;
+  // Staging layout for a 32 x WN bf16 block: 16-byte chunk q of row r at
+  // r * P + 16 * (q ^ f(r)) with a pitch and row hash that keep the 8-byte
+  // writes of 16 consecutive rows in distinct banks.
+  constexpr int NQ = WN / 8;                       // 16-byte chunks per row
+  constexpr int P = (NQ == 12) ? 208 : WN * 2;     // 96 columns: padded pitch
+  auto chunk_of = [&](int r, int q) {
+    if constexpr (NQ == 16) return q ^ (r & 15);
+    else if constexpr (NQ == 8) return q ^ ((r >> 1) & 7);
+    else return q;
+  };
+  static_assert(32 * P <= C::X_BYTES, "epilogue block must fit one token stage buffer");
+  int8_t* stage_buf = wave == 0 ? sX0 : wave == 1 ? sX1 : wave == 2 ? sX2 : sX3;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const bool full_rows = (N & 7) == 0;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int a = acc[i][j][4 * g + e];
+          if constexpr (W4) a >>= 4;
+          f[e] = (float(a) * sxv[j]) * swv[i][g][e];
+        }
+        const int q = i * 4 + g;  // 16-byte chunk holding columns 8q .. 8q+7
+        *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
+            make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes done
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < 32 * NQ / 64; ++k) {
+      const int id = lane + 64 * k;
+      const int r = id / NQ, q = id % NQ;
+      const int m = m0 + wm * WM + j * 32 + r;
+      const int n = n0 + wn * WN + 8 * q;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+      if (m < M) {
+        if (full_rows && n + 7 < N) {
+          *reinterpret_cast<uint4*>(y + int64_t(m) * N + n) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) y[int64_t(m) * N + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+    asm volatile("" ::: "memory");
   }
 }
 
