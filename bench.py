@@ -15,7 +15,7 @@ the launch stream), the rotate-quantize kernel's HBM bandwidth, and the CPU
 oracle timed on a bounded sample on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--profile {gemm,rq,copy,linear}]
+                       [--no-extras] [--profile {gemm,rq,rq_large,copy,linear}]
 """
 from __future__ import annotations
 
@@ -50,7 +50,12 @@ def kernel_source_hash(files):
 
 
 GEMM_SOURCES = ["w8a8_quantized_linear_amd/csrc/gemm_i8.hip"]
-RQ_SOURCES = ["w8a8_quantized_linear_amd/csrc/rotate_quant.hip"]
+RQ_SOURCES = ["w8a8_quantized_linear_amd/csrc/rotate_quant.hip",
+              "w8a8_quantized_linear_amd/csrc/rotate_quant_fast.hip"]
+# Rotate-quantize passes whose HBM fraction is the graded figure: the
+# 34 x 256-token stack's activations (K 4096 and the down projection's
+# K 12288) and the MLP down projection's input at M=2048.
+RQ_PASSES = [(8704, 4096), (8704, 12288), (2048, 12288)]
 
 
 def load_traffic(name, sources):
@@ -194,6 +199,34 @@ def extras_stack(torch, cr, wl, timer):
             "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
 
 
+def rq_passes(torch, cr, timer):
+    """Rotate-quantize bandwidth on the large passes, each cycled through
+    enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16)."""
+    dev = torch.device("cuda")
+    res = []
+    for (m, k) in RQ_PASSES:
+        per = m * (3 * k + 4)
+        n = max(2, -(-2 * MALL_BYTES // per) + 1)
+        g = torch.Generator(device=dev).manual_seed(m + k)
+        xs = [torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
+        qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
+        ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
+        t = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], m, k, GROUP, qs[i % n], ss[i % n]), 60, warm=5)
+        res.append({"M": m, "K": k, "us": round(t * 1e6, 2), "bytes": per,
+                    "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4)})
+        del xs, qs, ss
+    return res
+
+
+def copy_peak(torch, timer):
+    """Measured device-to-device copy bandwidth (1 GiB, read + write bytes)."""
+    a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    t = timer.time(lambda i: b.copy_(a), 10)
+    del a, b
+    return round(2 * (1 << 30) / t / 1e9, 1)
+
+
 def profile_mode(mode, torch, cr, wl):
     """Short runs for rocprofv3 counter collection (a handful of launches)."""
     dev = torch.device("cuda")
@@ -205,6 +238,16 @@ def profile_mode(mode, torch, cr, wl):
             b.copy_(a)
         torch.cuda.synchronize()
         log(f"copy calibration: 3 copies of {n} bytes")
+        return
+    if mode == "rq_large":
+        m, k = RQ_PASSES[1]
+        xd = torch.randn((m, k), device=dev).to(torch.bfloat16)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xs = torch.empty((m,), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            cr.convrot_rotate_quant(xd, m, k, GROUP, xq, xs)
+        torch.cuda.synchronize()
+        log(f"profile mode rq_large M={m} K={k}: 3 launches")
         return
     x, w, sets = build_sets(torch, cr, wl, 1)
     xd, wq, ws, y, wsp = sets[0]
@@ -227,7 +270,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "rq", "copy", "linear"], default=None)
+    ap.add_argument("--profile", choices=["gemm", "rq", "rq_large", "copy", "linear"], default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -336,6 +379,11 @@ def main():
         },
         "parity_rel_l2_sampled": rel,
     }
+    log("rotate-quantize on the large passes")
+    out["rotate_quant_large"] = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "passes": rq_passes(torch, cr, timer),
+                                 "traffic": load_traffic("rotate_quant_M8704_K12288", RQ_SOURCES),
+                                 "copy_peak_measured": copy_peak(torch, timer)}
     if not args.no_extras:
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)

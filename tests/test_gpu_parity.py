@@ -100,6 +100,34 @@ def test_rotate_quant_special_rows(lib):
     assert np.array_equal(xq, xq_ref)
 
 
+@pytest.mark.parametrize("K", [4096, 4352])
+def test_rotate_quant_tiny_rows(lib, K):
+    """Rows whose scale is far below 1: normal scales must match exactly as
+    for ordinary rows; where the oracle's fp32 scale is subnormal it carries
+    fewer bits, so codes may differ by 1 and scales by one subnormal step."""
+    say(f"rotate_quant tiny rows K={K}")
+    rng = np.random.default_rng(77)
+    x = np.zeros((5, K), dtype=np.float32)
+    x[0] = 1e-33                                   # constant groups, scale ~1e-35
+    x[1] = rng.standard_normal(K) * 1e-32          # random, scale ~1e-35 (normal)
+    x[2] = rng.standard_normal(K) * 1e-36          # scale near the subnormal edge
+    x[3, ::7] = 2.0 ** -130                        # bf16 subnormal entries
+    x[4] = rng.standard_normal(K)                  # an ordinary row beside them
+    xb = wl.float_to_bf16_bits(x)
+    xq, xs = lib.rotate_quant(bf16_to_dev(xb))
+    xq, xs = xq.cpu().numpy(), xs.cpu().numpy()
+    xq_ref, xs_ref = oracle.rotate_quant(xb, 256)
+    normal = xs_ref >= np.float32(2.0 ** -126)
+    assert normal[[0, 1, 4]].all()
+    assert_scales_close(xs[normal], xs_ref[normal])
+    assert_codes_close(xq[normal], xq_ref[normal])
+    assert np.array_equal(xq[0], xq_ref[0])
+    sub = ~normal
+    assert np.all(np.abs(xs[sub].astype(np.float64) - xs_ref[sub]) <= 2.0 ** -149 * 1.5)
+    assert np.abs(xq[sub].astype(np.int16) - xq_ref[sub]).max(initial=0) <= 1
+    assert np.all(np.abs(xq).max(axis=1) == 127)
+
+
 def test_rotate_quant_ties_half_away(lib):
     say("rotate_quant exact ties")
     import scipy.linalg

@@ -12,6 +12,12 @@ namespace convrot {
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g,
                                int8_t* codes, float* scale, hipStream_t stream);
 
+// Fast path for bf16 activations with group 256 (K a multiple of 1024 up to
+// 16384, except 5, 7, 9..11, 13..15 x 1024); returns hipErrorNotSupported
+// without launching for other shapes.
+hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* x_scale,
+                                    hipStream_t stream);
+
 // int4 weight preparation with the per-row clip search; clip_index may be null.
 hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,
                                      uint8_t* wq4, float* scale, int32_t* clip_index, hipStream_t stream);

@@ -296,6 +296,11 @@ hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* cod
 
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g, int8_t* codes,
                                float* scale, hipStream_t stream) {
+  if (in_dtype == IN_BF16 && log2g == 8) {
+    const hipError_t e =
+        launch_rotate_quant_g256(static_cast<const uint16_t*>(x), rows, K, codes, scale, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (in_dtype == IN_BF16) return dispatch<IN_BF16, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
   return dispatch<IN_F32, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
 }

@@ -1,0 +1,255 @@
+// Fast path of the activation rotate-and-quantize pass for group 256 (the
+// group size of ConvRot int8 checkpoints: "MOSS-Image Qwen3.5-9B text encoder,
+// INT8 (W8A8, ConvRot)", file table rows "Quantized" and "Matmul").
+//
+// One token row is held in the registers of TW wavefronts (TW = 1 for
+// K <= 4096); each lane owns C chunks of 16 consecutive bf16 values and a
+// group of 256 values lives in 16 consecutive lanes (one DPP row).  No LDS
+// and no barrier is needed when TW = 1.  Each wave loops over tokens and
+// fetches the next token's row while it transforms the current one.
+//
+// Walsh-Hadamard transform of a group (unnormalised; the 1/16 is a power of
+// two and is folded exactly into the scale):
+//   - element-index bits 0..3: butterflies inside the lane's 16 registers;
+//   - bits 4..7: butterflies between lanes, one v_fmac_f32_dpp per value and
+//     stage.  The four lane pairings are XOR 1, 2, 7 and 8 (DPP quad_perm,
+//     row_half_mirror, row_ror:8), a basis of GF(2)^4; lane i therefore loads
+//     and stores chunk u(i) = i ^ (bit 2 of i ? 3 : 0) of its group, which
+//     makes these pairings the standard Sylvester butterflies in u.  Every
+//     lane computes v + c * partner with c = +-1 by lane, so the values carry
+//     a known per-lane sign (-1)^popcount(u); it is applied for free in the
+//     quantization (the sign is folded into the reciprocal and the scale).
+//
+// Quantization per element (all fp32):
+//   scale = absmax / 127;  code = round_half_away(value / scale).
+// The quotient is the correctly rounded fp32 quotient, obtained from
+// q0 = v * r (r = 1/scale, correctly rounded), e = fma(-q0, scale, v),
+// q1 = fma(e, r, q0) (Markstein's correction), valid for scales in
+// [2^-100, 2^122) (rows with a smaller scale are lifted by 2^64 first);
+// half-away-from-zero rounding is trunc(q1 + copysign(0.49999997, q1)).
+// Both identities are checked exhaustively on the host
+// (tests/host/quotient_identities.c).
+#include "convrot_internal.h"
+
+namespace convrot {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// v += c * v[partner lane] for 16 registers, one DPP stage.  The s_nop
+// covers the DPP read-after-VALU-write hazard for values written just
+// before the block; inside the block each register is read once.
+#define CONVROT_DPP_STAGE(CTRL)                                                                        \
+  asm volatile("s_nop 1\n\t"                                                                           \
+               "v_fmac_f32_dpp %0, %0, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %1, %1, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %2, %2, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %3, %3, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %4, %4, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %5, %5, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %6, %6, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %7, %7, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %8, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %9, %9, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"      \
+               "v_fmac_f32_dpp %10, %10, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"    \
+               "v_fmac_f32_dpp %11, %11, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"    \
+               "v_fmac_f32_dpp %12, %12, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"    \
+               "v_fmac_f32_dpp %13, %13, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"    \
+               "v_fmac_f32_dpp %14, %14, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"    \
+               "v_fmac_f32_dpp %15, %15, %16 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"        \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),   \
+                 "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]),             \
+                 "+v"(v[13]), "+v"(v[14]), "+v"(v[15])                                                  \
+               : "v"(c))
+
+__device__ __forceinline__ void stage_xor1(float (&v)[16], float c) { CONVROT_DPP_STAGE("quad_perm:[1,0,3,2]"); }
+__device__ __forceinline__ void stage_xor2(float (&v)[16], float c) { CONVROT_DPP_STAGE("quad_perm:[2,3,0,1]"); }
+__device__ __forceinline__ void stage_xor7(float (&v)[16], float c) { CONVROT_DPP_STAGE("row_half_mirror"); }
+__device__ __forceinline__ void stage_xor8(float (&v)[16], float c) { CONVROT_DPP_STAGE("row_ror:8"); }
+#undef CONVROT_DPP_STAGE
+
+// Butterflies over element-index bits 1..3 inside one lane (bit 0 is done
+// while unpacking the bf16 pairs).
+__device__ __forceinline__ void fwht16_rest(float (&v)[16]) {
+#pragma unroll
+  for (int h = 2; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (!(i & h)) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
+// m = max(m, |a|, |b|) in one instruction (the operands come out of the DPP
+// asm blocks, so the compiler would otherwise add NaN-quieting moves).
+__device__ __forceinline__ void max3_abs(float& m, float a, float b) {
+  asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(m) : "v"(a), "v"(b));
+}
+
+// Byte-pack four int32 codes (each in [-127, 127]).
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+  const uint32_t lo = __builtin_amdgcn_perm(uint32_t(b), uint32_t(a), 0x0c0c0400u);  // a0 b0 0 0
+  const uint32_t hi = __builtin_amdgcn_perm(uint32_t(d), uint32_t(c), 0x0c0c0400u);  // c0 d0 0 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                                   // a0 b0 c0 d0
+}
+
+// round_half_away(n / d) for the correctly rounded fp32 quotient, given
+// r = RN(1/d) (both may carry the same sign flip).
+__device__ __forceinline__ int quantize(float n, float d, float r) {
+  const float q0 = n * r;
+  const float e = __builtin_fmaf(-q0, d, n);
+  const float q1 = __builtin_fmaf(e, r, q0);
+  const float half = __uint_as_float((__float_as_uint(q1) & 0x80000000u) | 0x3effffffu);  // +-0.49999997
+  return int(q1 + half);  // v_cvt_i32_f32 truncates
+}
+
+template <int C, int TW>
+__global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                     int K, int8_t* __restrict__ xq,
+                                                                     float* __restrict__ x_scale) {
+  static_assert(TW == 1 || TW == 2 || TW == 4, "waves per token");
+  constexpr int P = kWaves / TW;  // tokens per workgroup iteration
+  __shared__ float red[kWaves];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wt = wave % TW;  // this wave's index within its token
+  const int g = lane & 15;
+  // chunk of the group this lane loads and stores (see header)
+  const int u = g ^ ((g & 4) ? 3 : 0);
+  const int chunk_lane = (lane & ~15) + u;
+  // per-stage partner coefficients (-1)^u_k and the final sign (-1)^popcount(u)
+  const float c0 = (u & 1) ? -1.f : 1.f;
+  const float c1 = (u & 2) ? -1.f : 1.f;
+  const float c2 = (u & 4) ? -1.f : 1.f;
+  const float c3 = (u & 8) ? -1.f : 1.f;
+  const float sgn = c0 * c1 * c2 * c3;
+
+  const int64_t ngroups = (M + P - 1) / P;
+  // element offset of chunk j of this lane inside a token row
+  auto chunk_off = [&](int j) { return (j * (64 * TW) + wt * 64 + chunk_lane) * 16; };
+
+  u32x4 raw[C][2];
+  auto load = [&](int64_t tok) {
+    if (tok < M) {
+      const uint16_t* row = x + tok * K;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(row + chunk_off(j));
+        raw[j][0] = __builtin_nontemporal_load(p);
+        raw[j][1] = __builtin_nontemporal_load(p + 1);
+      }
+    }
+  };
+
+  int64_t grp = blockIdx.x;
+  load(grp * P + wave / TW);
+  for (; grp < ngroups; grp += gridDim.x) {
+    const int64_t tok = grp * P + wave / TW;
+    float v[C][16];
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const uint32_t w[8] = {raw[j][0][0], raw[j][0][1], raw[j][0][2], raw[j][0][3],
+                             raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {  // unpack a bf16 pair and do the bit-0 butterfly
+        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+        v[j][2 * i] = lo + hi;
+        v[j][2 * i + 1] = lo - hi;
+      }
+    }
+    // prefetch the next token of this wave while transforming this one
+    load((grp + gridDim.x) * P + wave / TW);
+
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      fwht16_rest(v[j]);
+      stage_xor1(v[j], c0);
+      stage_xor2(v[j], c1);
+      stage_xor7(v[j], c2);
+      stage_xor8(v[j], c3);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) max3_abs(amax, v[j][i], v[j][i + 1]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    if constexpr (TW > 1) {
+      if (lane == 0) red[wave] = amax;
+      __syncthreads();
+      const int first = (wave / TW) * TW;
+#pragma unroll
+      for (int w2 = 0; w2 < TW; ++w2) amax = fmaxf(amax, red[first + w2]);
+      __syncthreads();
+    }
+    float s = amax / 127.0f;  // scale of the unnormalised values
+    float out_mul = 0.0625f;  // 1/sqrt(256), exact
+    if (s < 0x1p-100f && s > 0.f) {
+      // Tiny row (the branch is uniform: amax is the token's).  Lift values
+      // and scale by 2^64 so 1/s stays finite and the quotient identity
+      // holds; for a normal s the quotients are exactly the unlifted ones.
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[j][i] *= 0x1p64f;
+      s = (amax * 0x1p64f) / 127.0f;
+      out_mul = 0x1p-68f;
+    }
+    const float r = s > 0.f ? 1.0f / s : 0.f;
+    const float ds = sgn * s, dr = sgn * r;  // fold the lane's sign into the quotient
+    if (tok < M) {
+      if (wt == 0 && lane == 0) x_scale[tok] = s * out_mul;
+      int8_t* out = xq + tok * K;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        int q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = quantize(v[j][i], ds, dr);
+        const u32x4 o = {pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
+                         pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + chunk_off(j)));
+      }
+    }
+  }
+}
+
+template <int C, int TW>
+hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, hipStream_t stream) {
+  constexpr int P = kWaves / TW;
+  const int64_t ngroups = (M + P - 1) / P;
+  // enough workgroups to keep every CU busy with several waves each; the
+  // rest is covered by the per-wave token loop
+  const int64_t max_blocks = 256 * 8;
+  const unsigned grid = unsigned(ngroups < max_blocks ? ngroups : max_blocks);
+  hipLaunchKernelGGL((rotate_quant_g256_kernel<C, TW>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K), xq, xs);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Returns hipErrorNotSupported (without launching) for shapes this path does
+// not cover; the caller then uses the general kernel.
+hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
+                                    hipStream_t stream) {
+  if (K % 1024 != 0) return hipErrorNotSupported;
+  switch (K / 1024) {
+    case 1: return launch<1, 1>(x, M, K, xq, xs, stream);
+    case 2: return launch<2, 1>(x, M, K, xq, xs, stream);
+    case 3: return launch<3, 1>(x, M, K, xq, xs, stream);
+    case 4: return launch<4, 1>(x, M, K, xq, xs, stream);
+    case 6: return launch<3, 2>(x, M, K, xq, xs, stream);
+    case 8: return launch<4, 2>(x, M, K, xq, xs, stream);
+    case 12: return launch<3, 4>(x, M, K, xq, xs, stream);
+    case 16: return launch<4, 4>(x, M, K, xq, xs, stream);
+    default: return hipErrorNotSupported;
+  }
+}
+
+}  // namespace convrot
