@@ -53,6 +53,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 namespace convrot {
 namespace {
@@ -463,6 +464,355 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_kernel(const int8_t* __re
   }
 }
 
+// ---------------------------------------------------------------------------
+// int8-weight kernel with 128-byte K stages.  Each row chunk of a stage is a
+// whole 128-byte cache line, which the global->LDS load path serves about
+// 1.6x faster than half lines (measured on gfx950: ~69 against ~44 B/clk
+// per CU).  Two LDS stages; per 128-K step one barrier:
+//   phase 1: K-slices 0..2 of stage kt, each slice's MFMAs interleaved with
+//            the LDS reads of the next slice (the first group also issues
+//            the tail of stage kt+1's loads); then wait for stage kt+1 and
+//            barrier;
+//   phase 2: slice 3 of stage kt (its fragments are already in registers),
+//            interleaved with the reads of stage kt+1's slice 0 and the
+//            loads of stage kt+2 into the buffer stage kt has just freed.
+// LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r is stored at
+// c ^ ((r >> 1) & 7), conflict-free for the fragment reads (measured).
+__device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
+
+template <int BM, int BN>
+struct Cfg8 {
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int TI = WN / 32, TJ = WM / 32;
+  static constexpr int KB = 128;                                   // K bytes per stage
+  static constexpr int W_BYTES = BN * KB, X_BYTES = BM * KB;
+  static constexpr int W_LOADS = W_BYTES / 4096, X_LOADS = X_BYTES / 4096;  // per wave
+  static constexpr int LOADS = W_LOADS + X_LOADS;
+  static constexpr int NM = TI * TJ;                               // MFMAs per slice
+  // The next-but-one stage's loads are spread over three slices of MFMAs:
+  // phase 2 (P2 loads), then the first two slices of the next phase 1
+  // (G0 and G1 loads), so the load path never sees more than about one
+  // wave-load per MFMA across the CU and the last load still has a slice
+  // of MFMAs before the wait.
+#ifndef CONVROT_SPLIT_DEN
+#define CONVROT_SPLIT_DEN 3
+#endif
+  static constexpr int P2 = (LOADS + CONVROT_SPLIT_DEN - 1) / CONVROT_SPLIT_DEN;
+  static constexpr int G0 = CONVROT_SPLIT_DEN == 1 ? 0 : (LOADS - P2 + CONVROT_SPLIT_DEN - 2) / (CONVROT_SPLIT_DEN - 1);
+  static constexpr int G1 = LOADS - P2 - G0;
+  static_assert(P2 <= NM && G0 <= NM && G1 <= NM && G1 >= 0, "at most one load per MFMA");
+  static constexpr int STAGE = W_BYTES + X_BYTES;
+  static_assert(W_LOADS * 4096 == W_BYTES && X_LOADS * 4096 == X_BYTES, "tile must split into 4 KB");
+  static_assert(LOADS < 64, "vmcnt budget");
+};
+
+template <int BM, int BN, bool EVEN>
+__device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx,
+                                               const int8_t* __restrict__ W, const float* __restrict__ sw, int M,
+                                               int N, int K, int tiles_m, int tiles_n,
+                                               int32_t* __restrict__ acc_out, uint16_t* __restrict__ y) {
+  using C = Cfg8<BM, BN>;
+  constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS, P2 = C::P2;
+  // Separate arrays per stage buffer: the compiler then knows that the
+  // global->LDS writes into one buffer do not alias reads of the other and
+  // keeps them interleaved.
+  __shared__ __attribute__((aligned(1024))) int8_t sW0[C::W_BYTES], sW1[C::W_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sX0[C::X_BYTES], sX1[C::X_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS targets stay scalar
+  const int wm = wave >> 1, wn = wave & 1;
+  const int row = lane & 31, half = lane >> 5;
+
+  const int T = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int tile_m = t % tiles_m, tile_n = t / tiles_m;
+  const int m0 = tile_m * BM, n0 = tile_n * BN;
+
+  const int rows_x = min(BM, M - m0), rows_w = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(X + int64_t(m0) * K), short(0), rows_x * K, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(W + int64_t(n0) * K), short(0), rows_w * K, kBufFlags);
+  // EVEN (K a multiple of 256, so the steps pair up with no partial stage):
+  // the stage's K offset goes into the instruction's scalar offset and each
+  // load is one scalar M0 update plus the load itself.  The prefetches of the
+  // two stages past K read the next rows or out-of-range zeros into buffers
+  // that are never consumed.  Otherwise every 16-byte chunk is range-checked
+  // per lane.
+
+  // Load block b (1 KB) holds rows 8b..8b+7; lane i writes LDS byte 16 i of
+  // the block, i.e. position i & 7 of row 8b + (i >> 3), which holds source
+  // chunk (i & 7) ^ swz128(row).
+  unsigned offw[C::W_LOADS], offx[C::X_LOADS];
+  int kw[C::W_LOADS], kx[C::X_LOADS];
+#pragma unroll
+  for (int j = 0; j < C::W_LOADS; ++j) {
+    const int r = (wave * C::W_LOADS + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz128(r);
+    kw[j] = 16 * c;
+    offw[j] = unsigned(r * K + 16 * c);
+  }
+#pragma unroll
+  for (int j = 0; j < C::X_LOADS; ++j) {
+    const int r = (wave * C::X_LOADS + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz128(r);
+    kx[j] = 16 * c;
+    offx[j] = unsigned(r * K + 16 * c);
+  }
+  // Loads of one stage in a fixed order (token blocks, then weight blocks);
+  // q selects which of them: [Q0, Q1).
+  auto issue = [&](int s, int k0, auto q0, auto q1) {
+    constexpr int Q0 = decltype(q0)::value, Q1 = decltype(q1)::value;
+    int8_t* const sW = s ? sW1 : sW0;
+    int8_t* const sX = s ? sX1 : sX0;
+#pragma unroll
+    for (int q = Q0; q < Q1; ++q) {
+      if (q < C::X_LOADS) {
+        const int j = q;
+        lds_ptr_t dst = (lds_ptr_t)(sX + (wave * C::X_LOADS + j) * 1024);
+        if constexpr (EVEN) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, offx[j], k0, 0, 0);
+        } else {
+          const unsigned off = (k0 + kx[j] < K) ? offx[j] + unsigned(k0) : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, off, 0, 0, 0);
+        }
+      } else {
+        const int j = q - C::X_LOADS;
+        lds_ptr_t dst = (lds_ptr_t)(sW + (wave * C::W_LOADS + j) * 1024);
+        if constexpr (EVEN) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, dst, 16, offw[j], k0, 0, 0);
+        } else {
+          const unsigned off = (k0 + kw[j] < K) ? offw[j] + unsigned(k0) : kOOB;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, dst, 16, off, 0, 0, 0);
+        }
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using IP2 = std::integral_constant<int, P2>;
+  using IG0 = std::integral_constant<int, P2 + C::G0>;
+  using IL = std::integral_constant<int, L>;
+
+  // Fragment addresses inside a stage for slice 0; slice sl is at addr ^ 32 sl.
+  int wadr[TI], xadr[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int r = wn * WN + i * 32 + row;
+    wadr[i] = r * 128 + 16 * (half ^ swz128(r));
+  }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int r = wm * WM + j * 32 + row;
+    xadr[j] = r * 128 + 16 * (half ^ swz128(r));
+  }
+
+  v4i fa[2][TI], fb[2][TJ];
+  auto read = [&](int s, int sl, int b) {
+    const int8_t* bw = s ? sW1 : sW0;
+    const int8_t* bx = s ? sX1 : sX0;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[b][i] = *reinterpret_cast<const v4i*>(bw + (wadr[i] ^ (32 * sl)));
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb[b][j] = *reinterpret_cast<const v4i*>(bx + (xadr[j] ^ (32 * sl)));
+  };
+
+  v16i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  auto mfma = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
+  };
+  auto sync_stage = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  constexpr int NM = C::NM, ND = TI + TJ;
+  const int ksteps = EVEN ? K / 128 : ((K + 127) / 128 + 1) & ~1;  // even: the loop body covers two steps
+
+  // Prologue: all of stage 0, the phase-2 share of stage 1.
+  issue(0, 0, I0{}, IL{});
+  issue(1, 128, I0{}, IP2{});
+  wait_vmcnt<P2>();
+  sync_stage();
+  read(0, 0, 0);
+
+  for (int kb = 0; kb < ksteps; kb += 2) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kt = kb + s;
+      // phase 1
+      read(s, 1, 1);
+      mfma(0);
+      issue(s ^ 1, (kt + 1) * 128, IP2{}, IG0{});
+      interleave_phase<NM, C::G0, ND>();
+      read(s, 2, 0);
+      mfma(1);
+      issue(s ^ 1, (kt + 1) * 128, IG0{}, IL{});
+      interleave_phase<NM, C::G1, ND>();
+      read(s, 3, 1);
+      mfma(0);
+      interleave_phase<NM, 0, ND>();
+      wait_vmcnt<0>();
+      sync_stage();
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2
+      issue(s, (kt + 2) * 128, I0{}, IP2{});
+      read(s ^ 1, 0, 0);
+      mfma(1);
+      interleave_phase<NM, P2, ND>();
+    }
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue (same scheme as the packed-weight kernel above).
+  float swv[TI][4][4];
+  float sxv[TJ];
+  if (y) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half + e;
+          swv[i][g][e] = n < N ? sw[n] : 0.f;
+        }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + j * 32 + row;
+      sxv[j] = m < M ? sx[m] : 0.f;
+    }
+  }
+  if (acc_out) {
+    const bool vec_ok = (N & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * WM + j * 32 + row;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
+          const int a[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+          if (vec_ok && n + 3 < N) {
+            *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = make_int4(a[0], a[1], a[2], a[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) acc_out[int64_t(m) * N + n + e] = a[e];
+          }
+        }
+    }
+  }
+  if (!y) return;
+  constexpr int NQ = WN / 8;
+  constexpr int P = (NQ == 12) ? 208 : WN * 2;
+  constexpr int STG = (32 * P + 1023) / 1024 * 1024;
+  static_assert(4 * STG <= (C::X_BYTES > C::W_BYTES ? C::X_BYTES : C::W_BYTES),
+                "epilogue staging must fit one stage buffer");
+  auto chunk_of = [&](int r, int q) {
+    if constexpr (NQ == 16) return q ^ (r & 15);
+    else if constexpr (NQ == 8) return q ^ ((r >> 1) & 7);
+    else return q;
+  };
+  int8_t* stage_buf = (C::X_BYTES >= C::W_BYTES ? sX0 : sW0) + wave * STG;
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  const bool full_rows = (N & 7) == 0;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = (float(acc[i][j][4 * g + e]) * sxv[j]) * swv[i][g][e];
+        const int q = i * 4 + g;
+        *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
+            make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < 32 * NQ / 64; ++k) {
+      const int id = lane + 64 * k;
+      const int r = id / NQ, q = id % NQ;
+      const int m = m0 + wm * WM + j * 32 + r;
+      const int n = n0 + wn * WN + 8 * q;
+      const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+      if (m < M) {
+        if (full_rows && n + 7 < N) {
+          *reinterpret_cast<uint4*>(y + int64_t(m) * N + n) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (n + e < N) y[int64_t(m) * N + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    asm volatile("" ::: "memory");
+  }
+}
+
+// K a multiple of 256 (every group-256 linear): unchecked scalar-offset loads.
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_kernel(const int8_t* __restrict__ X,
+                                                                   const float* __restrict__ sx,
+                                                                   const int8_t* __restrict__ W,
+                                                                   const float* __restrict__ sw, int M, int N, int K,
+                                                                   int tiles_m, int tiles_n,
+                                                                   int32_t* __restrict__ acc_out,
+                                                                   uint16_t* __restrict__ y) {
+  gemm_k128_body<BM, BN, true>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, acc_out, y);
+}
+
+// Any K (a multiple of 16): every 16-byte chunk range-checked.
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const int8_t* __restrict__ X,
+                                                                        const float* __restrict__ sx,
+                                                                        const int8_t* __restrict__ W,
+                                                                        const float* __restrict__ sw, int M, int N,
+                                                                        int K, int tiles_m, int tiles_n,
+                                                                        int32_t* __restrict__ acc_out,
+                                                                        uint16_t* __restrict__ y) {
+  gemm_k128_body<BM, BN, false>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, acc_out, y);
+}
+
+template <int BM, int BN>
+hipError_t launch_k128(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int M, int N,
+                       int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  const dim3 grid(unsigned(tiles_m) * unsigned(tiles_n));
+  void (*kernel)(const int8_t*, const float*, const int8_t*, const float*, int, int, int, int, int, int32_t*,
+                 uint16_t*) = gemm_i8_k128_tail_kernel<BM, BN>;
+  if (K % 256 == 0) kernel = gemm_i8_k128_kernel<BM, BN>;
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, xq, x_scale, wq, w_scale, M, N, K, tiles_m, tiles_n,
+                     acc_out, y);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, bool W4>
 hipError_t launch_cfg(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M,
                       int N, int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
@@ -517,6 +867,14 @@ hipError_t launch_w(const int8_t* xq, const float* x_scale, const uint8_t* wq, c
                     int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
   TileChoice tc = tile_override();
   if (tc.bm == 0 || (W4 && tc.bn == 192)) tc = choose_tile(M, N, W4);
+  if constexpr (!W4) {
+    const int8_t* w8 = reinterpret_cast<const int8_t*>(wq);
+    if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+    if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+    if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+    if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+    return launch_k128<128, 128>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+  }
   if (tc.bm == 256 && tc.bn == 256) return launch_cfg<256, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
   if constexpr (!W4)
     if (tc.bm == 256 && tc.bn == 192) return launch_cfg<256, 192, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
