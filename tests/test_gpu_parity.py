@@ -37,6 +37,26 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
     assert np.array_equal(bf16_from_dev(y), oracle.epilogue(acc_ref, xs, ws))
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 12288, 512), (8704, 4096, 256), (2048, 4096, 768)])
+def test_gemm_i8_large_sampled(lib, M, N, K):
+    """Shapes whose tile plan uses the large tiles and, at M=2048 N=12288, two
+    column bands; int32 accumulators bit-exact on sampled rows (all columns,
+    so every band boundary is covered) against an int64 product."""
+    say(f"gemm_i8 W8 large M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    a = rng.integers(-127, 128, (M, K), dtype=np.int8)
+    b = rng.integers(-127, 128, (N, K), dtype=np.int8)
+    xs = (rng.random(M) * 0.1 + 1e-3).astype(np.float32)
+    ws = (rng.random(N) * 1e-3 + 1e-5).astype(np.float32)
+    acc, y = lib.gemm_i8(to_dev(a), to_dev(xs), to_dev(b), to_dev(ws), wbits=8)
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, 255, 256, M - 1]]))
+    ref = a[rows].astype(np.int64) @ b.astype(np.int64).T
+    got = acc[rows.tolist()].cpu().numpy()
+    assert np.array_equal(got, ref)
+    yref = oracle.epilogue(ref.astype(np.int32), xs[rows], ws)
+    assert np.array_equal(bf16_from_dev(y[rows.tolist()]), yref)
+
+
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 256, 512), (33, 70, 224), (130, 257, 4096), (64, 12288, 4096)])
 def test_gemm_w4_bit_exact(lib, M, N, K):
     say(f"gemm_i8 W4 M={M} N={N} K={K}")

@@ -509,7 +509,7 @@ struct Cfg8 {
 template <int BM, int BN, bool EVEN>
 __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx,
                                                const int8_t* __restrict__ W, const float* __restrict__ sw, int M,
-                                               int N, int K, int tiles_m, int tiles_n,
+                                               int N, int K, int tiles_m, int tiles_n, int ldy,
                                                int32_t* __restrict__ acc_out, uint16_t* __restrict__ y) {
   using C = Cfg8<BM, BN>;
   constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS, P2 = C::P2;
@@ -518,6 +518,8 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // keeps them interleaved.
   __shared__ __attribute__((aligned(1024))) int8_t sW0[C::W_BYTES], sW1[C::W_BYTES];
   __shared__ __attribute__((aligned(1024))) int8_t sX0[C::X_BYTES], sX1[C::X_BYTES];
+  // This tile's weight-row and token scales (rows past N / M read as zero).
+  __shared__ __attribute__((aligned(1024))) float sSw[256], sSx[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -644,7 +646,17 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   constexpr int NM = C::NM, ND = TI + TJ;
   const int ksteps = EVEN ? K / 128 : ((K + 127) / 128 + 1) & ~1;  // even: the loop body covers two steps
 
-  // Prologue: all of stage 0, the phase-2 share of stage 1.
+  // Prologue: the scales (one 1 KB load each, by waves 0 and 1; first
+  // used in the epilogue, long after the main loop's waits), all of stage
+  // 0, the phase-2 share of stage 1.
+  if (y && wave < 2) {
+    const float* src = wave == 0 ? sw + n0 : sx + m0;
+    const int nrec = 4 * (wave == 0 ? rows_w : rows_x);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
+                                                                        kBufFlags);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(wave == 0 ? sSw : sSx), 16, unsigned(lane * 16), 0,
+                                             0, 0);
+  }
   issue(0, 0, I0{}, IL{});
   issue(1, 128, I0{}, IP2{});
   wait_vmcnt<P2>();
@@ -679,25 +691,12 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   }
   wait_vmcnt<0>();
 
-  // Epilogue (same scheme as the packed-weight kernel above).
-  float swv[TI][4][4];
-  float sxv[TJ];
-  if (y) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half + e;
-          swv[i][g][e] = n < N ? sw[n] : 0.f;
-        }
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int m = m0 + wm * WM + j * 32 + row;
-      sxv[j] = m < M ? sx[m] : 0.f;
-    }
-  }
+  // Epilogue.  Block (i, j): lane holds token m = ... + (lane & 31) and
+  // weight rows n = ... + 8 g + 4 (lane >> 5) + (0..3) in accumulators
+  // 4g..4g+3.  The bf16 results of one 32-token block at a time are staged
+  // in LDS and leave as 16-byte row-contiguous stores (from the accumulator
+  // layout a store would scatter 8-byte pieces over 32 rows).  Scales come
+  // from LDS, four weight scales per read.
   if (acc_out) {
     const bool vec_ok = (N & 3) == 0;
 #pragma unroll
@@ -711,11 +710,11 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
           const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
           const int a[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
           if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<int4*>(acc_out + int64_t(m) * N + n) = make_int4(a[0], a[1], a[2], a[3]);
+            *reinterpret_cast<int4*>(acc_out + int64_t(m) * ldy + n) = make_int4(a[0], a[1], a[2], a[3]);
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (n + e < N) acc_out[int64_t(m) * N + n + e] = a[e];
+              if (n + e < N) acc_out[int64_t(m) * ldy + n + e] = a[e];
           }
         }
     }
@@ -736,37 +735,52 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  const bool full_rows = (N & 7) == 0;
+  // Interior tiles (and N a multiple of 8) store without per-element checks.
+  const bool interior = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
+  const float* swt = sSw + wn * WN + 4 * half;
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
+    const float sxj = sSx[wm * WM + j * 32 + row];
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float f[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = (float(acc[i][j][4 * g + e]) * sxv[j]) * swv[i][g][e];
+        const float4 sw4 = *reinterpret_cast<const float4*>(swt + i * 32 + 8 * g);
+        const float f0 = (float(acc[i][j][4 * g + 0]) * sxj) * sw4.x;
+        const float f1 = (float(acc[i][j][4 * g + 1]) * sxj) * sw4.y;
+        const float f2 = (float(acc[i][j][4 * g + 2]) * sxj) * sw4.z;
+        const float f3 = (float(acc[i][j][4 * g + 3]) * sxj) * sw4.w;
         const int q = i * 4 + g;
         *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
-            make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+            make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
       }
     __builtin_amdgcn_s_waitcnt(0xc07f);
     asm volatile("" ::: "memory");
+    if (interior) {
 #pragma unroll
-    for (int k = 0; k < 32 * NQ / 64; ++k) {
-      const int id = lane + 64 * k;
-      const int r = id / NQ, q = id % NQ;
-      const int m = m0 + wm * WM + j * 32 + r;
-      const int n = n0 + wn * WN + 8 * q;
-      const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
-      if (m < M) {
-        if (full_rows && n + 7 < N) {
-          *reinterpret_cast<uint4*>(y + int64_t(m) * N + n) = v;
-        } else {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int k = 0; k < 32 * NQ / 64; ++k) {
+        const int id = lane + 64 * k;
+        const int r = id / NQ, q = id % NQ;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+        *reinterpret_cast<uint4*>(y + int64_t(m0 + wm * WM + j * 32 + r) * ldy + (n0 + wn * WN + 8 * q)) = v;
+      }
+    } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (n + e < N) y[int64_t(m) * N + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+      for (int k = 0; k < 32 * NQ / 64; ++k) {
+        const int id = lane + 64 * k;
+        const int r = id / NQ, q = id % NQ;
+        const int m = m0 + wm * WM + j * 32 + r;
+        const int n = n0 + wn * WN + 8 * q;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+        if (m < M) {
+          if ((N & 7) == 0 && n + 7 < N) {
+            *reinterpret_cast<uint4*>(y + int64_t(m) * ldy + n) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (n + e < N) y[int64_t(m) * ldy + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+          }
         }
       }
     }
@@ -781,10 +795,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_kernel(const int8_t*
                                                                    const float* __restrict__ sx,
                                                                    const int8_t* __restrict__ W,
                                                                    const float* __restrict__ sw, int M, int N, int K,
-                                                                   int tiles_m, int tiles_n,
+                                                                   int tiles_m, int tiles_n, int ldy,
                                                                    int32_t* __restrict__ acc_out,
                                                                    uint16_t* __restrict__ y) {
-  gemm_k128_body<BM, BN, true>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, acc_out, y);
+  gemm_k128_body<BM, BN, true>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, ldy, acc_out, y);
 }
 
 // Any K (a multiple of 16): every 16-byte chunk range-checked.
@@ -793,23 +807,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const in
                                                                         const float* __restrict__ sx,
                                                                         const int8_t* __restrict__ W,
                                                                         const float* __restrict__ sw, int M, int N,
-                                                                        int K, int tiles_m, int tiles_n,
+                                                                        int K, int tiles_m, int tiles_n, int ldy,
                                                                         int32_t* __restrict__ acc_out,
                                                                         uint16_t* __restrict__ y) {
-  gemm_k128_body<BM, BN, false>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, acc_out, y);
+  gemm_k128_body<BM, BN, false>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, ldy, acc_out, y);
 }
 
+// One band of output columns: y and acc_out have row stride ldy; wq,
+// w_scale, acc_out and y already point at the band's first column.
 template <int BM, int BN>
 hipError_t launch_k128(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int M, int N,
-                       int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+                       int K, int ldy, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
   const dim3 grid(unsigned(tiles_m) * unsigned(tiles_n));
-  void (*kernel)(const int8_t*, const float*, const int8_t*, const float*, int, int, int, int, int, int32_t*,
+  void (*kernel)(const int8_t*, const float*, const int8_t*, const float*, int, int, int, int, int, int, int32_t*,
                  uint16_t*) = gemm_i8_k128_tail_kernel<BM, BN>;
   if (K % 256 == 0) kernel = gemm_i8_k128_kernel<BM, BN>;
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, xq, x_scale, wq, w_scale, M, N, K, tiles_m, tiles_n,
-                     acc_out, y);
+                     ldy, acc_out, y);
   return hipGetLastError();
 }
 
@@ -862,34 +878,97 @@ TileChoice tile_override() {
   return forced;
 }
 
-template <bool W4>
-hipError_t launch_w(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M, int N,
-                    int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
-  TileChoice tc = tile_override();
-  if (tc.bm == 0 || (W4 && tc.bn == 192)) tc = choose_tile(M, N, W4);
-  if constexpr (!W4) {
-    const int8_t* w8 = reinterpret_cast<const int8_t*>(wq);
-    if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
-    if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
-    if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
-    if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
-    return launch_k128<128, 128>(xq, x_scale, w8, w_scale, M, N, K, acc_out, y, stream);
+// A plan for int8 weights: up to two bands of output columns, each with its
+// own tile shape (launched back to back on the stream; the chooser below
+// uses one band, the override can ask for two).
+struct Band {
+  int n_cols;  // 0 = the rest of N
+  TileChoice tc;
+};
+struct Plan {
+  int nb;
+  Band b[2];
+};
+
+// Tile plan for int8 weights, from measurements on MI355X under sustained
+// load.  The chip runs this GEMM below its top clock, and the clock rises
+// when less data moves per MFMA, so the largest tile (256x256: fewest
+// L2->LDS bytes per operation) wins once it fills several whole rounds of
+// the 256 CUs; otherwise 256x192 when it fills at least three quarters of a
+// round, and 128x128 for small problems (more CUs busy).  Splitting N into
+// bands of different tiles to even out a partial round measured no faster
+// than a single 256x192 launch (the second launch waits for the first).
+Plan choose_plan(int64_t M, int64_t N) {
+  const int cus = 256;
+  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+  if (N % 256 == 0 && tiles(256, 256) >= 3 * cus) return {1, {{0, {256, 256}}, {0, {0, 0}}}};
+  if (4 * tiles(256, 192) >= 3 * cus) return {1, {{0, {256, 192}}, {0, {0, 0}}}};
+  return {1, {{0, {128, 128}}, {0, {0, 0}}}};
+}
+
+// CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan (a tuning
+// override for sweeps; every plan gives bit-identical results).
+bool plan_override(Plan& out) {
+  static const Plan forced = [] {
+    Plan p{0, {{0, {0, 0}}, {0, {0, 0}}}};
+    const char* s = getenv("CONVROT_GEMM_PLAN");
+    if (!s) return p;
+    int bm0, bn0, cols = 0, bm1, bn1;
+    if (sscanf(s, "%dx%d:%d,%dx%d", &bm0, &bn0, &cols, &bm1, &bn1) == 5) return Plan{2, {{cols, {bm0, bn0}}, {0, {bm1, bn1}}}};
+    if (sscanf(s, "%dx%d", &bm0, &bn0) == 2) return Plan{1, {{0, {bm0, bn0}}, {0, {0, 0}}}};
+    return p;
+  }();
+  if (forced.nb == 0) return false;
+  out = forced;
+  return true;
+}
+
+hipError_t launch_band8(TileChoice tc, const int8_t* xq, const float* x_scale, const int8_t* wq,
+                        const float* w_scale, int M, int N, int K, int ldy, int32_t* acc_out, uint16_t* y,
+                        hipStream_t stream) {
+  if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+  if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+  return launch_k128<128, 128>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+}
+
+hipError_t launch_w8(const int8_t* xq, const float* x_scale, const int8_t* wq, const float* w_scale, int M, int N,
+                     int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  Plan plan;
+  const TileChoice forced = tile_override();
+  if (!plan_override(plan)) plan = forced.bm ? Plan{1, {{0, forced}, {0, {0, 0}}}} : choose_plan(M, N);
+  int n_begin = 0;
+  for (int i = 0; i < plan.nb && n_begin < N; ++i) {
+    const int cols = (plan.b[i].n_cols > 0 && n_begin + plan.b[i].n_cols < N) ? plan.b[i].n_cols : N - n_begin;
+    const hipError_t e = launch_band8(plan.b[i].tc, xq, x_scale, wq + int64_t(n_begin) * K,
+                                      w_scale ? w_scale + n_begin : nullptr, M, cols, K, N,
+                                      acc_out ? acc_out + n_begin : nullptr, y ? y + n_begin : nullptr, stream);
+    if (e != hipSuccess) return e;
+    n_begin += cols;
   }
-  if (tc.bm == 256 && tc.bn == 256) return launch_cfg<256, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
-  if constexpr (!W4)
-    if (tc.bm == 256 && tc.bn == 192) return launch_cfg<256, 192, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
-  if (tc.bm == 256 && tc.bn == 128) return launch_cfg<256, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
-  if (tc.bm == 128 && tc.bn == 256) return launch_cfg<128, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
-  return launch_cfg<128, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  return hipSuccess;
+}
+
+hipError_t launch_w4(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M, int N,
+                     int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+  TileChoice tc = tile_override();
+  if (tc.bm == 0 || tc.bn == 192) tc = choose_tile(M, N, true);
+  if (tc.bm == 256 && tc.bn == 256) return launch_cfg<256, 256, true>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_cfg<256, 128, true>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  if (tc.bm == 128 && tc.bn == 256) return launch_cfg<128, 256, true>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
+  return launch_cfg<128, 128, true>(xq, x_scale, wq, w_scale, M, N, K, acc_out, y, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
-  const uint8_t* W = static_cast<const uint8_t*>(wq);
-  if (wbits == 4) return launch_w<true>(xq, x_scale, W, w_scale, int(M), int(N), int(K), acc_out, y, stream);
-  return launch_w<false>(xq, x_scale, W, w_scale, int(M), int(N), int(K), acc_out, y, stream);
+  if (wbits == 4)
+    return launch_w4(xq, x_scale, static_cast<const uint8_t*>(wq), w_scale, int(M), int(N), int(K), acc_out, y,
+                     stream);
+  return launch_w8(xq, x_scale, static_cast<const int8_t*>(wq), w_scale, int(M), int(N), int(K), acc_out, y,
+                   stream);
 }
 
 }  // namespace convrot
