@@ -181,10 +181,8 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
       const_cast<uint8_t*>(W + int64_t(n0) * Kb), short(0), rows_w * Kb, kBufFlags);
   // EVEN (K a multiple of 256, so the steps pair up with no partial stage):
   // the stage's K offset goes into the instruction's scalar offset and each
-  // load is one scalar M0 update plus the load itself.  The prefetches of the
-  // two stages past K read the next rows or out-of-range zeros into buffers
-  // that are never consumed.  Otherwise every 16-byte chunk is range-checked
-  // per lane.
+  // load is one scalar M0 update plus the load itself.  Otherwise every
+  // 16-byte chunk is range-checked per lane.
 
   // Load block b (1 KB) holds rows 8b..8b+7 of 128-byte rows (16b..16b+15
   // of 64-byte packed int4 rows); lane i writes LDS byte 16 i of the block,
@@ -213,19 +211,28 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     kx[j] = 16 * c;
     offx[j] = unsigned(r * K + 16 * c);
   }
+  // Descriptors with no records: the loop's prefetches of the stages past
+  // the end of K go through them, so they read zeros without touching memory.
+  const __amdgpu_buffer_rsrc_t rsx0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X), short(0), 0,
+                                                                        kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsw0 = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W), short(0), 0,
+                                                                        kBufFlags);
   // Loads of one stage in a fixed order (token blocks, then weight blocks);
   // q selects which of them: [Q0, Q1).
   auto issue = [&](int s, int k0, auto q0, auto q1) {
     constexpr int Q0 = decltype(q0)::value, Q1 = decltype(q1)::value;
     int8_t* const sW = s ? sW1 : sW0;
     int8_t* const sX = s ? sX1 : sX0;
+    const bool live = k0 < K;  // uniform
+    const __amdgpu_buffer_rsrc_t rx = live ? rsx : rsx0;
+    const __amdgpu_buffer_rsrc_t rw = live ? rsw : rsw0;
 #pragma unroll
     for (int q = Q0; q < Q1; ++q) {
       if (q < C::X_LOADS) {
         const int j = q;
         lds_ptr_t dst = (lds_ptr_t)(sX + (wave * C::X_LOADS + j) * 1024);
         if constexpr (EVEN) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, offx[j], k0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, dst, 16, offx[j], k0, 0, 0);
         } else {
           const unsigned off = (k0 + kx[j] < K) ? offx[j] + unsigned(k0) : kOOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, dst, 16, off, 0, 0, 0);
@@ -235,7 +242,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         lds_ptr_t dst = (lds_ptr_t)(sW + (wave * C::W_LOADS + j) * 1024);
         const int kwb = W4 ? k0 / 2 : k0;  // byte offset of the stage in a weight row
         if constexpr (EVEN) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, dst, 16, offw[j], kwb, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, dst, 16, offw[j], kwb, 0, 0);
         } else {
           const unsigned off = (k0 + kw[j] < K) ? offw[j] + unsigned(kwb) : kOOB;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, dst, 16, off, 0, 0, 0);
