@@ -144,6 +144,11 @@ struct CfgK {
   static_assert(P2 <= NM && G0 <= NM, "at most one load per MFMA");
   static_assert(W_LOADS * 4096 == W_BYTES && X_LOADS * 4096 == X_BYTES, "tile must split into 4 KB");
   static_assert(LOADS < 64, "vmcnt budget");
+  // Persistent tile walk (the next tile's first loads overlap this tile's
+  // epilogue).  Not for 256x256: 256 accumulators per lane leave no room to
+  // keep the loop-invariant load offsets live across the epilogue, and the
+  // spills cost more than the overlap gains (measured).
+  static constexpr bool PERSIST = !(BM == 256 && BN == 256);
 };
 
 template <int BM, int BN, bool W4, bool EVEN>
@@ -168,17 +173,27 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   const int wm = wave >> 1, wn = wave & 1;
   const int row = lane & 31, half = lane >> 5;
 
+  // Persistent tiles: workgroup b takes tiles v = b, b + G, ... in an
+  // XCD-aware order (the initial dispatch puts workgroup b on XCD b % 8, so
+  // for G a multiple of 8 every tile of b lies in XCD b % 8's contiguous
+  // block of tiles, which share weight and token rows in its L2).
   const int T = tiles_m * tiles_n;
-  int t = blockIdx.x;
-  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int tile_m = t % tiles_m, tile_n = t / tiles_m;
-  const int m0 = tile_m * BM, n0 = tile_n * BN;
+  const int G = gridDim.x;
+  auto tile_of = [&](int v) { return (T & 7) == 0 ? (v & 7) * (T >> 3) + (v >> 3) : v; };
 
-  const int rows_x = min(BM, M - m0), rows_w = min(BN, N - n0);
-  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int8_t*>(X + int64_t(m0) * K), short(0), rows_x * K, kBufFlags);
-  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(W + int64_t(n0) * Kb), short(0), rows_w * Kb, kBufFlags);
+  int m0 = 0, n0 = 0, rows_x = 0, rows_w = 0;
+  __amdgpu_buffer_rsrc_t rsx, rsw;
+  auto set_tile = [&](int v) {
+    const int t = tile_of(v);
+    m0 = (t % tiles_m) * BM;
+    n0 = (t / tiles_m) * BN;
+    rows_x = min(BM, M - m0);
+    rows_w = min(BN, N - n0);
+    rsx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + int64_t(m0) * K), short(0), rows_x * K,
+                                            kBufFlags);
+    rsw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + int64_t(n0) * Kb), short(0), rows_w * Kb,
+                                            kBufFlags);
+  };
   // EVEN (K a multiple of 256, so the steps pair up with no partial stage):
   // the stage's K offset goes into the instruction's scalar offset and each
   // load is one scalar M0 update plus the load itself.  Otherwise every
@@ -300,13 +315,6 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   };
 
   v16i acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
-
   auto mfma = [&](int b) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
@@ -326,147 +334,196 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   constexpr int NM = C::NM, ND0 = TI + TJ, ND1 = W4 ? TJ : TI + TJ;
   const int ksteps = EVEN ? K / 128 : ((K + 127) / 128 + 1) & ~1;  // even: the loop body covers two steps
 
-  // Prologue: the scales (one 1 KB load each, by waves 0 and 1; first
-  // used in the epilogue, long after the main loop's waits), all of stage
-  // 0, the phase-2 share of stage 1.
-  if (y && wave < 2) {
-    const float* src = wave == 0 ? sw + n0 : sx + m0;
-    const int nrec = 4 * (wave == 0 ? rows_w : rows_x);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
-                                                                        kBufFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(wave == 0 ? sSw : sSx), 16, unsigned(lane * 16), 0,
-                                             0, 0);
-  }
+  // Epilogue staging: a dedicated LDS area when it fits beside the stage
+  // buffers (then both of the next tile's first loads can go out before the
+  // epilogue), else the stage-1 arrays (then only stage 0's).
+  constexpr int NQ = WN / 8;
+  constexpr int P = (NQ == 12) ? 208 : WN * 2;
+  constexpr int STG = (32 * P + 1023) / 1024 * 1024;
+  constexpr bool DEDICATED = BM == 256 && 2 * (C::W_BYTES + C::X_BYTES) + 2048 + 4 * STG <= 160 * 1024;
+  __shared__ __attribute__((aligned(1024))) int8_t sStg[DEDICATED ? 4 * STG : 16];
+  static_assert(DEDICATED || 2 * STG <= C::X_BYTES, "two staging blocks must fit the stage-1 token array");
+  static_assert(DEDICATED || 2 * STG <= C::W_BYTES, "two staging blocks must fit the stage-1 weight array");
+  int8_t* const stage_buf = DEDICATED ? sStg + wave * STG : (wave < 2 ? sX1 : sW1) + (wave & 1) * STG;
+
+  // The tile's weight-row and token scales go to LDS with one 1 KB load each
+  // (waves 0 and 1); they are first read in the epilogue.
+  auto load_scales = [&]() {
+    if (y && wave < 2) {
+      const float* src = wave == 0 ? sw + n0 : sx + m0;
+      const int nrec = 4 * (wave == 0 ? rows_w : rows_x);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
+                                                                          kBufFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(wave == 0 ? sSw : sSx), 16, unsigned(lane * 16), 0,
+                                               0, 0);
+    }
+  };
+
+  // First tile: scales, all of stage 0, the phase-2 share of stage 1.
+  int v = blockIdx.x;
+  set_tile(v);
+  load_scales();
   issue(0, 0, I0{}, IL{});
   issue(1, 128, I0{}, IP2{});
   wait_vmcnt<P2>();
   sync_stage();
-  read(0, 0, 0);
 
-  for (int kb = 0; kb < ksteps; kb += 2) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kt = kb + s;
-      // phase 1
-      read(s, 1, 1);
-      mfma(0);
-      issue(s ^ 1, (kt + 1) * 128, IP2{}, IL{});
-      interleave_phase<NM, C::G0, ND1>();
-      read(s, 2, 0);
-      mfma(1);
-      interleave_phase<NM, 0, ND0>();
-      read(s, 3, 1);
-      mfma(0);
-      interleave_phase<NM, 0, ND1>();
-      wait_vmcnt<0>();
-      sync_stage();
-      __builtin_amdgcn_sched_barrier(0);
-      // phase 2
-      issue(s, (kt + 2) * 128, I0{}, IP2{});
-      read(s ^ 1, 0, 0);
-      mfma(1);
-      interleave_phase<NM, P2, ND0>();
-    }
-  }
-  wait_vmcnt<0>();
-
-  // Epilogue.  Block (i, j): lane holds token m = ... + (lane & 31) and
-  // weight rows n = ... + 8 g + 4 (lane >> 5) + (0..3) in accumulators
-  // 4g..4g+3.  The bf16 results of one 32-token block at a time are staged
-  // in LDS and leave as 16-byte row-contiguous stores (from the accumulator
-  // layout a store would scatter 8-byte pieces over 32 rows).  Scales come
-  // from LDS, four weight scales per read.
-  if (acc_out) {
-    const bool vec_ok = (N & 3) == 0;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      const int m = m0 + wm * WM + j * 32 + row;
-      if (m >= M) continue;
-#pragma unroll
-      for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
-          constexpr int sh = W4 ? 4 : 0;  // int4 weights accumulate 16 x the product
-          const int a[4] = {acc[i][j][4 * g] >> sh, acc[i][j][4 * g + 1] >> sh, acc[i][j][4 * g + 2] >> sh,
-                            acc[i][j][4 * g + 3] >> sh};
-          if (vec_ok && n + 3 < N) {
-            *reinterpret_cast<int4*>(acc_out + int64_t(m) * ldy + n) = make_int4(a[0], a[1], a[2], a[3]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (n + e < N) acc_out[int64_t(m) * ldy + n + e] = a[e];
-          }
-        }
-    }
-  }
-  if (!y) return;
-  constexpr int NQ = WN / 8;
-  constexpr int P = (NQ == 12) ? 208 : WN * 2;
-  constexpr int STG = (32 * P + 1023) / 1024 * 1024;
-  static_assert(STG <= C::X_BYTES && STG <= C::W_BYTES, "a wave's staging block must fit one stage array");
-  auto chunk_of = [&](int r, int q) {
-    if constexpr (NQ == 16) return q ^ (r & 15);
-    else if constexpr (NQ == 8) return q ^ ((r >> 1) & 7);
-    else return q;
-  };
-  int8_t* stage_buf = wave == 0 ? sX0 : wave == 1 ? sX1 : wave == 2 ? sW0 : sW1;  // one array per wave
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  // Interior tiles (and N a multiple of 8) store without per-element checks.
-  const bool interior = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
-  const float* swt = sSw + wn * WN + 4 * half;
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const float sxj = sSx[wm * WM + j * 32 + row];
+  for (;;) {
+    read(0, 0, 0);
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 sw4 = *reinterpret_cast<const float4*>(swt + i * 32 + 8 * g);
-        constexpr int sh = W4 ? 4 : 0;
-        const float f0 = (float(acc[i][j][4 * g + 0] >> sh) * sxj) * sw4.x;
-        const float f1 = (float(acc[i][j][4 * g + 1] >> sh) * sxj) * sw4.y;
-        const float f2 = (float(acc[i][j][4 * g + 2] >> sh) * sxj) * sw4.z;
-        const float f3 = (float(acc[i][j][4 * g + 3] >> sh) * sxj) * sw4.w;
-        const int q = i * 4 + g;
-        *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
-            make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
-      }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    asm volatile("" ::: "memory");
-    if (interior) {
+      for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int k = 0; k < 32 * NQ / 64; ++k) {
-        const int id = lane + 64 * k;
-        const int r = id / NQ, q = id % NQ;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
-        *reinterpret_cast<uint4*>(y + int64_t(m0 + wm * WM + j * 32 + r) * ldy + (n0 + wn * WN + 8 * q)) = v;
-      }
-    } else {
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+    for (int kb = 0; kb < ksteps; kb += 2) {
 #pragma unroll
-      for (int k = 0; k < 32 * NQ / 64; ++k) {
-        const int id = lane + 64 * k;
-        const int r = id / NQ, q = id % NQ;
-        const int m = m0 + wm * WM + j * 32 + r;
-        const int n = n0 + wn * WN + 8 * q;
-        const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
-        if (m < M) {
-          if ((N & 7) == 0 && n + 7 < N) {
-            *reinterpret_cast<uint4*>(y + int64_t(m) * ldy + n) = v;
-          } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (n + e < N) y[int64_t(m) * ldy + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
-          }
-        }
+      for (int s = 0; s < 2; ++s) {
+        const int kt = kb + s;
+        // phase 1
+        read(s, 1, 1);
+        mfma(0);
+        issue(s ^ 1, (kt + 1) * 128, IP2{}, IL{});
+        interleave_phase<NM, C::G0, ND1>();
+        read(s, 2, 0);
+        mfma(1);
+        interleave_phase<NM, 0, ND0>();
+        read(s, 3, 1);
+        mfma(0);
+        interleave_phase<NM, 0, ND1>();
+        wait_vmcnt<0>();
+        sync_stage();
+        __builtin_amdgcn_sched_barrier(0);
+        // phase 2
+        issue(s, (kt + 2) * 128, I0{}, IP2{});
+        read(s ^ 1, 0, 0);
+        mfma(1);
+        interleave_phase<NM, P2, ND0>();
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    sync_stage();  // every wave is done with both stage buffers
+
+    // Start the next tile's loads so that they land during this epilogue.
+    const int em0 = m0, en0 = n0;
+    const int vn = v + G;
+    const bool more = C::PERSIST && vn < T;
+    if (more) {
+      set_tile(vn);
+      issue(0, 0, I0{}, IL{});
+      if constexpr (DEDICATED) issue(1, 128, I0{}, IP2{});
+    }
+
+    // Epilogue.  Block (i, j): lane holds token m = ... + (lane & 31) and
+    // weight rows n = ... + 8 g + 4 (lane >> 5) + (0..3) in accumulators
+    // 4g..4g+3.  The bf16 results of one 32-token block at a time are staged
+    // in LDS and leave as 16-byte row-contiguous stores (from the accumulator
+    // layout a store would scatter 8-byte pieces over 32 rows).  Scales come
+    // from LDS, four weight scales per read.
+    {
+      const int m0 = em0, n0 = en0;
+    if (acc_out) {
+      const bool vec_ok = (N & 3) == 0;
+  #pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int m = m0 + wm * WM + j * 32 + row;
+        if (m >= M) continue;
+  #pragma unroll
+        for (int i = 0; i < TI; ++i)
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WN + i * 32 + 8 * g + 4 * half;
+            constexpr int sh = W4 ? 4 : 0;  // int4 weights accumulate 16 x the product
+            const int a[4] = {acc[i][j][4 * g] >> sh, acc[i][j][4 * g + 1] >> sh, acc[i][j][4 * g + 2] >> sh,
+                              acc[i][j][4 * g + 3] >> sh};
+            if (vec_ok && n + 3 < N) {
+              *reinterpret_cast<int4*>(acc_out + int64_t(m) * ldy + n) = make_int4(a[0], a[1], a[2], a[3]);
+            } else {
+  #pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (n + e < N) acc_out[int64_t(m) * ldy + n + e] = a[e];
+            }
+          }
+      }
+    }
+      if (y) {
+        auto chunk_of = [&](int r, int q) {
+          if constexpr (NQ == 16) return q ^ (r & 15);
+          else if constexpr (NQ == 8) return q ^ ((r >> 1) & 7);
+          else return q;
+        };
+        // Interior tiles (and N a multiple of 8) store without per-element checks.
+        const bool interior = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
+        const float* swt = sSw + wn * WN + 4 * half;
+    #pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const float sxj = sSx[wm * WM + j * 32 + row];
+    #pragma unroll
+        for (int i = 0; i < TI; ++i)
+    #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 sw4 = *reinterpret_cast<const float4*>(swt + i * 32 + 8 * g);
+            constexpr int sh = W4 ? 4 : 0;
+            const float f0 = (float(acc[i][j][4 * g + 0] >> sh) * sxj) * sw4.x;
+            const float f1 = (float(acc[i][j][4 * g + 1] >> sh) * sxj) * sw4.y;
+            const float f2 = (float(acc[i][j][4 * g + 2] >> sh) * sxj) * sw4.z;
+            const float f3 = (float(acc[i][j][4 * g + 3] >> sh) * sxj) * sw4.w;
+            const int q = i * 4 + g;
+            *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
+                make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
+          }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        asm volatile("" ::: "memory");
+        if (interior) {
+    #pragma unroll
+          for (int k = 0; k < 32 * NQ / 64; ++k) {
+            const int id = lane + 64 * k;
+            const int r = id / NQ, q = id % NQ;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+            *reinterpret_cast<uint4*>(y + int64_t(m0 + wm * WM + j * 32 + r) * ldy + (n0 + wn * WN + 8 * q)) = v;
+          }
+        } else {
+    #pragma unroll
+          for (int k = 0; k < 32 * NQ / 64; ++k) {
+            const int id = lane + 64 * k;
+            const int r = id / NQ, q = id % NQ;
+            const int m = m0 + wm * WM + j * 32 + r;
+            const int n = n0 + wn * WN + 8 * q;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
+            if (m < M) {
+              if ((N & 7) == 0 && n + 7 < N) {
+                *reinterpret_cast<uint4*>(y + int64_t(m) * ldy + n) = v;
+              } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    #pragma unroll
+                for (int e = 0; e < 8; ++e)
+                  if (n + e < N) y[int64_t(m) * ldy + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+              }
+            }
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        asm volatile("" ::: "memory");
+      }
+      }
+    }
+    if (!more) break;
+
+    // Next tile: its scales (this epilogue has finished reading the old ones),
+    // the rest of its first loads, then wait until stage 0 has landed.
+    // Loads and stores retire in issue order, so at most the loads issued
+    // after stage 0 may still be outstanding.
+    v = vn;
+    sync_stage();
+    load_scales();
+    if constexpr (DEDICATED) {
+      wait_vmcnt<1>();
+    } else {
+      issue(1, 128, I0{}, IP2{});
+      wait_vmcnt<P2>();
+    }
+    sync_stage();
   }
 }
 
@@ -494,6 +551,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const in
   gemm_k128_body<BM, BN, W4, false>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, ldy, acc_out, y);
 }
 
+// Workgroups of `kernel` the current device runs at once: compute units x
+// resident workgroups per unit, a multiple of 8 on MI355X (256 units, one or
+// two per unit), so the persistent tile order stays XCD-aware.  Cached per
+// device and kernel; 0 on error.
+int resident_slots(const void* kernel) {
+  struct Entry {
+    const void* kernel;
+    int device, slots;
+  };
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].slots;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
+  const int slots = cus * (per_cu > 0 ? per_cu : 1);
+  if (used < 64) cache[used++] = {kernel, dev, slots};
+  return slots;
+}
+
 // One band of output columns: y and acc_out have row stride ldy; wq,
 // w_scale, acc_out and y already point at the band's first column.
 template <int BM, int BN, bool W4>
@@ -501,10 +581,19 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, const uint8_t* wq
                        int K, int ldy, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  const dim3 grid(unsigned(tiles_m) * unsigned(tiles_n));
   void (*kernel)(const int8_t*, const float*, const uint8_t*, const float*, int, int, int, int, int, int, int32_t*,
                  uint16_t*) = gemm_i8_k128_tail_kernel<BM, BN, W4>;
   if (K % 256 == 0) kernel = gemm_i8_k128_kernel<BM, BN, W4>;
+  // Persistent configurations: as many workgroups as the device holds at
+  // once (never more than there are tiles), each walking its tiles in turn;
+  // otherwise one workgroup per tile.
+  const int64_t tiles = int64_t(tiles_m) * tiles_n;
+  int64_t slots = tiles;
+  if (CfgK<BM, BN, W4>::PERSIST) {
+    slots = resident_slots(reinterpret_cast<const void*>(kernel));
+    if (slots <= 0) return hipErrorInvalidDeviceFunction;
+  }
+  const dim3 grid(unsigned(tiles < slots ? tiles : slots));
   hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, xq, x_scale, wq, w_scale, M, N, K, tiles_m, tiles_n,
                      ldy, acc_out, y);
   return hipGetLastError();
