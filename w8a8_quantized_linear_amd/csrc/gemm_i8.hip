@@ -420,7 +420,11 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     // 4g..4g+3.  The bf16 results of one 32-token block at a time are staged
     // in LDS and leave as 16-byte row-contiguous stores (from the accumulator
     // layout a store would scatter 8-byte pieces over 32 rows).  Scales come
-    // from LDS, four weight scales per read.
+    // from LDS, four weight scales per read.  Each wave stages in its own
+    // region and a wave's LDS operations execute in order, so no wait is
+    // needed between a block's staging writes and its reads, nor before the
+    // next block overwrites the region: the next block's arithmetic overlaps
+    // this block's LDS round trip and stores.
     {
       const int m0 = em0, n0 = en0;
     if (acc_out) {
@@ -473,8 +477,6 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
             *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
                 make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
           }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        asm volatile("" ::: "memory");
         if (interior) {
     #pragma unroll
           for (int k = 0; k < 32 * NQ / 64; ++k) {
@@ -503,8 +505,6 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
             }
           }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        asm volatile("" ::: "memory");
       }
       }
     }
