@@ -363,7 +363,7 @@ def main():
         "hot_tops": round(ops / t_hot / 1e12, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_i8_kernel (int8 MFMA GEMM + bf16 epilogue)",
+            "kernel": "gemm_i8_k128_kernel (int8 MFMA GEMM + bf16 epilogue)",
             "achieved": round(gemm_tops, 2),
             "peak": PEAK_INT8_TOPS,
             "unit": "TOPS",
