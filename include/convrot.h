@@ -29,9 +29,10 @@
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
  *    values are passed as their raw 16-bit patterns (uint16_t).
  *  - The caller owns every buffer and the stream.  The library never
- *    allocates or frees device memory, keeps no pointer after returning and
- *    has no mutable global state: calls on different streams may run
- *    concurrently.
+ *    allocates or frees device memory and keeps no pointer after returning;
+ *    its only global state is a lock-guarded memo of how many workgroups of
+ *    each kernel a device holds at once.  Calls from several host threads
+ *    and on different streams may run concurrently.
  *  - Work is enqueued on `stream` (0 = the null stream) without any host
  *    synchronisation; results are valid once the stream has reached them.
  *  - Arguments are validated on the host before anything is enqueued; on a

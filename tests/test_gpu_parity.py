@@ -358,3 +358,43 @@ def test_stack_config_sampled(lib):
             worst = max(worst, r)
             del w_dev, wq, ws, y
         say(f"C4: layer {layer} ok (worst rel L2 so far {worst:.2e})")
+
+
+def test_concurrent_host_threads(lib):
+    """Two host threads, each on its own stream, launching GEMMs of several
+    tile plans at once (first calls included, so the per-kernel occupancy
+    memo is filled concurrently): results stay bit-exact."""
+    import threading
+    import torch
+    say("gemm_i8 from two host threads on two streams")
+    # plans: 128x128 persistent, 256x192 persistent, range-checked K, 256x256
+    shapes = [(512, 4096, 512), (2048, 12288, 256), (300, 1000, 1040), (8704, 12288, 256)]
+    errors = []
+
+    def worker(idx):
+        try:
+            stream = torch.cuda.Stream()
+            rng = np.random.default_rng(500 + idx)
+            with torch.cuda.stream(stream):
+                for rep in range(3):
+                    for (M, N, K) in shapes[idx::2] + shapes[1 - idx::2]:
+                        a = rng.integers(-127, 128, (M, K), dtype=np.int8)
+                        b = rng.integers(-127, 128, (N, K), dtype=np.int8)
+                        xs = np.ones(M, np.float32)
+                        ws = np.ones(N, np.float32)
+                        acc, _ = lib.gemm_i8(to_dev(a), to_dev(xs), to_dev(b), to_dev(ws), wbits=8, want_y=False)
+                        stream.synchronize()
+                        rows = rng.choice(M, 8, replace=False)
+                        ref = a[rows].astype(np.int64) @ b.astype(np.int64).T
+                        if not np.array_equal(acc[rows.tolist()].cpu().numpy(), ref):
+                            errors.append((idx, M, N, K, rep))
+        except Exception as e:  # reported below
+            errors.append((idx, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    assert not errors, errors

@@ -53,6 +53,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 namespace convrot {
@@ -553,23 +554,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const in
 
 // Workgroups of `kernel` the current device runs at once: compute units x
 // resident workgroups per unit, a multiple of 8 on MI355X (256 units, one or
-// two per unit), so the persistent tile order stays XCD-aware.  Cached per
-// device and kernel; 0 on error.
+// two per unit), so the persistent tile order stays XCD-aware.  Memoised per
+// device and kernel (a read-only fact of the device, guarded for calls from
+// several host threads); 0 on error.
 int resident_slots(const void* kernel) {
   struct Entry {
     const void* kernel;
     int device, slots;
   };
+  static std::mutex mu;
   static Entry cache[64];
   static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
-  for (int i = 0; i < used; ++i)
-    if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].slots;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].slots;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
   const int slots = cus * (per_cu > 0 ? per_cu : 1);
+  std::lock_guard<std::mutex> lock(mu);
   if (used < 64) cache[used++] = {kernel, dev, slots};
   return slots;
 }
