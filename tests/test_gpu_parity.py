@@ -37,18 +37,33 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
     assert np.array_equal(bf16_from_dev(y), oracle.epilogue(acc_ref, xs, ws))
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 12288, 512), (8704, 4096, 256), (2048, 4096, 768)])
-def test_gemm_i8_large_sampled(lib, M, N, K):
-    """Shapes whose tile plan uses the large tiles and, at M=2048 N=12288, two
-    column bands; int32 accumulators bit-exact on sampled rows (all columns,
-    so every band boundary is covered) against an int64 product."""
-    say(f"gemm_i8 W8 large M={M} N={N} K={K}")
-    rng = np.random.default_rng(M + N + K)
+@pytest.mark.parametrize("wbits,M,N,K", [
+    (8, 2048, 12288, 512),   # 256x192, persistent
+    (8, 8704, 4096, 256),    # 256x192, three tiles per workgroup
+    (8, 2048, 4096, 768),    # 128x128
+    (8, 2000, 12280, 512),   # 256x192, ragged M and N (N not a multiple of 8)
+    (8, 8700, 12288, 256),   # 256x256, ragged M
+    (4, 2048, 12288, 512),   # packed int4, 256x192
+    (4, 4000, 12288, 256),   # packed int4, 256x256, ragged M
+])
+def test_gemm_i8_large_sampled(lib, wbits, M, N, K):
+    """Shapes whose tile plan uses the large tiles (persistent or not),
+    including ragged edges; int32 accumulators bit-exact on sampled rows
+    (all columns) against an int64 product, bf16 outputs bit-exact against
+    the oracle's epilogue."""
+    say(f"gemm_i8 W{wbits} large M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K + wbits)
     a = rng.integers(-127, 128, (M, K), dtype=np.int8)
-    b = rng.integers(-127, 128, (N, K), dtype=np.int8)
     xs = (rng.random(M) * 0.1 + 1e-3).astype(np.float32)
     ws = (rng.random(N) * 1e-3 + 1e-5).astype(np.float32)
-    acc, y = lib.gemm_i8(to_dev(a), to_dev(xs), to_dev(b), to_dev(ws), wbits=8)
+    if wbits == 8:
+        b = rng.integers(-127, 128, (N, K), dtype=np.int8)
+        wdev = to_dev(b)
+    else:
+        packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        b = oracle.unpack_i4(packed)
+        wdev = to_dev(packed)
+    acc, y = lib.gemm_i8(to_dev(a), to_dev(xs), wdev, to_dev(ws), wbits=wbits)
     rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, 255, 256, M - 1]]))
     ref = a[rows].astype(np.int64) @ b.astype(np.int64).T
     got = acc[rows.tolist()].cpu().numpy()
