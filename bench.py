@@ -279,7 +279,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the ConvRot linear runs on a single MI355X); "
+        print("bench.py: measures one GPU only (each ConvRot linear runs on a single MI355X); "
               "multi-GPU runs are not supported", file=sys.stderr)
         sys.exit(2)
 

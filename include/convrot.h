@@ -40,7 +40,8 @@
  *    successful no-op.
  *  - Tensor pointers must be 16-byte aligned; scale pointers 4-byte aligned.
  *  - Shapes: K % 16 == 0, K % group == 0, K <= CONVROT_MAX_K; int4 weights
- *    additionally need K % 32 == 0.  group must be a power of two in
+ *    additionally need K % 32 == 0.  The calls that multiply (the linears
+ *    and convrot_gemm_i8) accept M, N <= 2^30.  group must be a power of two in
  *    [1, 256]; group 1 means no rotation (plain row-wise int8).  Unlike the
  *    converter described on "qwen3vl_8b_int8_convrot" ("Layer and group
  *    selection"), the library never silently falls back to group 1 when K is
@@ -64,7 +65,7 @@ extern "C" {
 enum convrot_status {
   CONVROT_OK = 0,
   CONVROT_ERR_NULL = 1,      /* a required pointer is NULL */
-  CONVROT_ERR_SHAPE = 2,     /* M < 0, N <= 0, K <= 0, K % 16, K % group, K odd/%32 for int4, K too large */
+  CONVROT_ERR_SHAPE = 2,     /* M < 0, N <= 0, K <= 0, K % 16, K % group, K % 32 for int4, K or M/N too large */
   CONVROT_ERR_GROUP = 3,     /* group is not a power of two in [1, 256] */
   CONVROT_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
   CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than convrot_workspace_size() */

@@ -117,6 +117,7 @@ def test_linear_validation(L):
     assert lin8(A, 8, 512, B, C, 64, 100, D, E, need) == ERR["group"]
     assert lin4(A, 8, 528, B, C, 64, 16, D, E, need) == ERR["shape"]   # int4 needs K % 32
     assert lin8(NUL, 0, 512, NUL, NUL, 64, 256, NUL, NUL, 0) == 0
+    assert lin8(A, 1 << 31, 512, B, C, 64, 256, D, E, need) == ERR["shape"]
 
 
 def test_quantize_weight_validation(L):
@@ -138,3 +139,6 @@ def test_gemm_validation(L):
     assert gemm(A, B, C, 4, D, 4, 4, 48, E, NUL) == ERR["shape"]
     assert gemm(A, B, C, 8, D, 4, 4, 64, MIS, NUL) == ERR["align"]
     assert gemm(NUL, NUL, NUL, 8, NUL, 0, 4, 64, NUL, NUL) == 0
+    big = (1 << 30) + 1                                              # 32-bit tile indexing bound
+    assert gemm(A, B, C, 8, D, big, 4, 64, E, NUL) == ERR["shape"]
+    assert gemm(A, B, C, 8, D, 4, big, 64, E, NUL) == ERR["shape"]

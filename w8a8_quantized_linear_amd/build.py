@@ -52,10 +52,25 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    _check_defined(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def _check_defined(lib: str) -> None:
+    """Fail the build if the library leaves any of its own symbols undefined
+    (for instance a kernel's host-side stub that the compiler did not emit):
+    such a library would only fail later, when it is loaded."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    missing = [line.split()[-1] for line in r.stdout.splitlines() if "convrot" in line]
+    if missing:
+        os.remove(lib)
+        raise RuntimeError("link left library symbols undefined:\n  " + "\n  ".join(missing))
 
 
 if __name__ == "__main__":

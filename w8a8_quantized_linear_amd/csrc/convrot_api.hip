@@ -30,6 +30,9 @@ int check_k(int64_t K, int group, bool int4) {
 
 int device_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_DEVICE; }
 
+// The GEMM indexes tiles, rows and columns with 32-bit integers.
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
 }  // namespace
 
 extern "C" {
@@ -41,7 +44,8 @@ const char* convrot_status_string(int status) {
     case CONVROT_OK: return "ok";
     case CONVROT_ERR_NULL: return "a required pointer is NULL";
     case CONVROT_ERR_SHAPE: return "invalid shape (need M >= 0, N > 0, K > 0, K % 16 == 0, K % group == 0, "
-                                   "K <= 32768, and K % 32 == 0 for int4 weights)";
+                                   "K <= 32768, K % 32 == 0 for int4 weights, and M, N <= 2^30 for the "
+                                   "product)";
     case CONVROT_ERR_GROUP: return "group must be a power of two in [1, 256]";
     case CONVROT_ERR_ALIGN: return "tensor pointers must be 16-byte aligned (scales 4-byte aligned)";
     case CONVROT_ERR_WORKSPACE: return "workspace smaller than convrot_workspace_size(M, K)";
@@ -104,6 +108,7 @@ int convrot_gemm_i8(const int8_t* xq, const float* x_scale, const void* wq, int 
   if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || K > CONVROT_MAX_K || (wbits == 4 && K % 32 != 0))
     return CONVROT_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows) return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!xq || !wq || (!acc_out && !y)) return CONVROT_ERR_NULL;
   if (y && (!x_scale || !w_scale)) return CONVROT_ERR_NULL;
@@ -117,7 +122,7 @@ static int linear_impl(const uint16_t* x, int64_t M, int64_t K, const void* wq, 
                        int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   if (int rc = check_k(K, group, wbits == 4)) return rc;
-  if (M < 0 || N <= 0) return CONVROT_ERR_SHAPE;
+  if (M < 0 || N <= 0 || M > kMaxRows || N > kMaxRows) return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!x || !wq || !w_scale || !y || !workspace) return CONVROT_ERR_NULL;
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
