@@ -460,15 +460,26 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         };
         // Interior tiles (and N a multiple of 8) store without per-element checks.
         const bool interior = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
-        const float* swt = sSw + wn * WN + 4 * half;
+        // All scales this lane needs, read once: the staging writes below go
+        // through a per-wave pointer the compiler cannot separate from the
+        // scale arrays, so reads inside the block loop would be repeated.
+        float4 sw4s[TI][4];
+        float sxv[TJ];
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + wn * WN + 4 * half + i * 32 + 8 * g);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * WM + j * 32 + row];
     #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const float sxj = sSx[wm * WM + j * 32 + row];
+        const float sxj = sxv[j];
     #pragma unroll
         for (int i = 0; i < TI; ++i)
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float4 sw4 = *reinterpret_cast<const float4*>(swt + i * 32 + 8 * g);
+            const float4 sw4 = sw4s[i][g];
             constexpr int sh = W4 ? 4 : 0;
             const float f0 = (float(acc[i][j][4 * g + 0] >> sh) * sxj) * sw4.x;
             const float f1 = (float(acc[i][j][4 * g + 1] >> sh) * sxj) * sw4.y;
