@@ -68,6 +68,8 @@ def _load():
         "oracle_quantize_weight_i4": (I, [P, I64, I64, I, P, P, P]),
         "oracle_unpack_i4": (I, [P, I64, I64, P]),
         "oracle_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P]),
+        "oracle_rmsnorm_bf16": (I, [P, P, ctypes.c_float, I64, I64, P]),
+        "oracle_rmsnorm_rotate_quant": (I, [P, P, ctypes.c_float, I64, I64, I, P, P, P]),
         "oracle_num_threads": (I, []),
     }
     for name, (res, args) in sigs.items():
@@ -203,3 +205,28 @@ def w4a8_linear(x_bf16: np.ndarray, wq4: np.ndarray, w_scale: np.ndarray, group:
     _check(_load().oracle_w4a8_linear(_ptr(x), M, K, _ptr(wq4), _ptr(ws), N, int(group), _ptr(y)),
            "w4a8_linear")
     return y
+
+
+def rmsnorm(x_bf16: np.ndarray, w: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm with (1 + w) weights: bf16 bits [M, K], fp32 [K] -> bf16 bits [M, K]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    M, K = x.shape
+    assert w.shape == (K,)
+    y = np.empty((M, K), dtype=np.uint16)
+    _check(_load().oracle_rmsnorm_bf16(_ptr(x), _ptr(w), float(eps), M, K, _ptr(y)), "rmsnorm")
+    return y
+
+
+def rmsnorm_rotate_quant(x_bf16: np.ndarray, w: np.ndarray, eps: float = 1e-6, group: int = 256):
+    """RMSNorm, then rotate + quantize its bf16 output -> (xq int8, x_scale fp32, y bf16 bits)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    M, K = x.shape
+    assert w.shape == (K,)
+    xq = np.empty((M, K), dtype=np.int8)
+    s = np.empty(M, dtype=np.float32)
+    y = np.empty((M, K), dtype=np.uint16)
+    _check(_load().oracle_rmsnorm_rotate_quant(_ptr(x), _ptr(w), float(eps), M, K, int(group), _ptr(xq), _ptr(s),
+                                               _ptr(y)), "rmsnorm_rotate_quant")
+    return xq, s, y

@@ -37,6 +37,11 @@
  *    0.01; scale = c * absmax / 7; the c with the smallest sum of squared
  *    reconstruction error wins (ties to the larger c); byte j of a row holds
  *    column 2j in its low nibble and column 2j+1 in its high nibble.
+ *  - RMSNorm before the linear ([P1] rows "Changed" and "How it was made":
+ *    SmoothQuant scales folded into the norm weight as (1 + w) / s - 1): the
+ *    norm multiplies by (1 + w); mean square over the whole row, eps inside
+ *    the square root; fp32 arithmetic except the fp64 sum of squares; the
+ *    output is rounded to bf16 (the activation dtype) before it is rotated.
  *
  * Build: gcc -std=c11 -O2 -fopenmp -ffp-contract=off -shared -fPIC.
  * OpenMP is used only to run independent rows in parallel; every row is
@@ -360,6 +365,49 @@ int oracle_w4a8_linear(const uint16_t *x, int64_t M, int64_t K, const uint8_t *w
     int rc = wq ? oracle_unpack_i4(wq4, N, K, wq) : ORACLE_ERR_ARG;
     if (rc == ORACLE_OK) rc = oracle_w8a8_linear(x, M, K, wq, w_scale, N, g, y);
     free(wq);
+    return rc;
+}
+
+/* ------------------------------------------------------------- RMSNorm */
+
+/* The decoder-layer RMSNorm that precedes the quantized linears ([P1] table
+ * row "Changed": its weights carry the SmoothQuant scales; "How it was made":
+ * the scales are folded into the norm as (1 + w) / s - 1, i.e. the norm
+ * multiplies by (1 + w)).  Per row of x bf16 [M,K]:
+ *   ms = (float)(sum_k x_k^2 / K)   (the sum in fp64: every x_k^2 of a bf16
+ *                                    value is exact there)
+ *   r  = 1 / sqrt(ms + eps)         (fp32, each operation rounded)
+ *   y_k = bf16_rne((x_k * r) * (1 + w_k))  (fp32, in this order)
+ * The output is bf16, the activation dtype the linear's input has.  Every
+ * step is fp32 except the sum, so a GPU that accumulates in fp64 as well
+ * reaches the same bf16 values. */
+int oracle_rmsnorm_bf16(const uint16_t *x, const float *w, float eps, int64_t M, int64_t K, uint16_t *y) {
+    if (!x || !w || !y || M < 0 || K <= 0 || !(eps >= 0.0f)) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t *xr = x + m * K;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = bf16_bits_to_double(xr[k]);
+            ss += v * v;
+        }
+        const float ms = (float)(ss / (double)K);
+        const float r = 1.0f / sqrtf(ms + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            const float t = (float)bf16_bits_to_double(xr[k]) * r;
+            const float u = t * (1.0f + w[k]);
+            y[m * K + k] = float_to_bf16_rne(u);
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* RMSNorm followed by the activation rotate + quantization of its bf16
+ * output: what the linear after a norm sees. */
+int oracle_rmsnorm_rotate_quant(const uint16_t *x, const float *w, float eps, int64_t M, int64_t K, int g,
+                                int8_t *xq, float *x_scale, uint16_t *y) {
+    int rc = oracle_rmsnorm_bf16(x, w, eps, M, K, y);
+    if (rc == ORACLE_OK) rc = oracle_rotate_quant(y, M, K, g, xq, x_scale);
     return rc;
 }
 

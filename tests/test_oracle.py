@@ -469,3 +469,83 @@ def test_format_facts(oracle_mod):
     assert wq.dtype == np.int8 and ws.dtype == np.float32 and ws.shape == (8,)
     wq4, s4, _ = oracle_mod.quantize_weight_i4(w, g)
     assert wq4.shape[1] * facts["int4_weight"]["codes_per_byte"] == 2 * g
+
+
+# ------------------------------------------------------------------ RMSNorm
+# The norm that precedes the quantized linears multiplies by (1 + w) (the
+# SmoothQuant folding (1 + w) / s - 1 of "MOSS-Image ... INT8", "How it was
+# made").  The pins use powers of two so that every product and square root
+# along the way is exact and the expected bf16 value is fixed by hand.
+
+def test_rmsnorm_constant_power_of_two_rows(oracle_mod):
+    """A constant row c = +-2^k has rms |c|: with eps 0 and w 0 it normalises
+    to +-1 exactly."""
+    K = 512
+    vals = [2.0 ** k for k in range(-12, 13, 3)] + [-(2.0 ** k) for k in range(-9, 10, 3)]
+    x = np.array([[v] * K for v in vals], dtype=np.float32)
+    y = wl.bf16_bits_to_float(oracle_mod.rmsnorm(bf16(x), np.zeros(K, np.float32), eps=0.0))
+    assert np.array_equal(y, np.sign(x))
+
+
+@pytest.mark.parametrize("K", [256, 1024, 4096])
+def test_rmsnorm_one_hot_gives_sqrt_k(oracle_mod, K):
+    """A single nonzero a = 2^k has mean square a^2 / K: the normalised value
+    is sqrt(K) (a power of two for these K), every other entry 0."""
+    rng = np.random.default_rng(K)
+    x = np.zeros((6, K), np.float32)
+    pos = rng.choice(K, 6, replace=False)
+    for r, p in enumerate(pos):
+        x[r, p] = (-1) ** r * 2.0 ** (r - 3)
+    y = wl.bf16_bits_to_float(oracle_mod.rmsnorm(bf16(x), np.zeros(K, np.float32), eps=0.0))
+    expect = np.zeros_like(x)
+    expect[np.arange(6), pos] = np.sign(x[np.arange(6), pos]) * np.sqrt(K)
+    assert np.array_equal(y, expect)
+
+
+def test_rmsnorm_weight_enters_as_one_plus_w(oracle_mod):
+    """w = 1 and w = 3 scale the output by exactly 2 and 4; w = -1 zeroes it."""
+    rng = np.random.default_rng(5)
+    K = 256
+    xb = bf16(rng.standard_normal((4, K)).astype(np.float32))
+    y0 = wl.bf16_bits_to_float(oracle_mod.rmsnorm(xb, np.zeros(K, np.float32), 1e-6))
+    w = np.zeros(K, np.float32)
+    w[: K // 3] = 1.0
+    w[K // 3: 2 * K // 3] = 3.0
+    w[2 * K // 3:] = -1.0
+    y = wl.bf16_bits_to_float(oracle_mod.rmsnorm(xb, w, 1e-6))
+    assert np.array_equal(y, y0 * (1.0 + w))
+
+
+def test_rmsnorm_eps_inside_the_root(oracle_mod):
+    """Constant row c = 2^k with eps = c^2: the root is sqrt(2) c, so every
+    output is bf16(1/sqrt(2)) = 0.70703125."""
+    K = 256
+    for k in (-4, 0, 5):
+        c = 2.0 ** k
+        x = np.full((1, K), c, np.float32)
+        y = wl.bf16_bits_to_float(oracle_mod.rmsnorm(bf16(x), np.zeros(K, np.float32), eps=c * c))
+        assert np.all(y == np.float32(0.70703125)), (k, y[0, :2])
+
+
+def test_rmsnorm_zero_row_and_unit_rms(oracle_mod):
+    """A zero row stays zero (eps > 0); ordinary rows come out with mean
+    square 1 up to bf16 rounding."""
+    rng = np.random.default_rng(6)
+    K = 4096
+    x = (rng.standard_normal((8, K)) * 7.0).astype(np.float32)
+    x[0] = 0.0
+    y = wl.bf16_bits_to_float(oracle_mod.rmsnorm(bf16(x), np.zeros(K, np.float32), 1e-6)).astype(np.float64)
+    assert np.all(y[0] == 0.0)
+    ms = (y[1:] ** 2).mean(axis=1)
+    assert np.all(np.abs(ms - 1.0) < 5e-3), ms
+
+
+def test_rmsnorm_rotate_quant_is_the_composition(oracle_mod):
+    rng = np.random.default_rng(7)
+    K = 1024
+    xb = _rand_bf16(rng, 5, K, outliers=4)
+    w = (rng.standard_normal(K) * 0.3).astype(np.float32)
+    xq, s, y = oracle_mod.rmsnorm_rotate_quant(xb, w, 1e-6, 256)
+    assert np.array_equal(y, oracle_mod.rmsnorm(xb, w, 1e-6))
+    xq2, s2 = oracle_mod.rotate_quant(y, 256)
+    assert np.array_equal(xq, xq2) and np.array_equal(s, s2)
