@@ -70,7 +70,8 @@ enum convrot_status {
   CONVROT_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
   CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than convrot_workspace_size() */
   CONVROT_ERR_DEVICE = 6,    /* the HIP runtime reported an error while enqueueing */
-  CONVROT_ERR_DTYPE = 7      /* unsupported w_dtype or bits value */
+  CONVROT_ERR_DTYPE = 7,     /* unsupported w_dtype or bits value */
+  CONVROT_ERR_ARG = 8        /* a scalar argument is out of range (eps negative, NaN or infinite) */
 };
 
 /* Weight dtypes accepted by convrot_quantize_weight. */
@@ -106,6 +107,34 @@ int convrot_quantize_weight(const void *w, int w_dtype, int64_t N, int64_t K, in
  */
 int convrot_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int group, int8_t *xq, float *x_scale,
                          hipStream_t stream);
+
+/*
+ * convrot_rmsnorm_rotate_quant -- the RMSNorm that feeds a linear, fused with
+ * its rotation + per-token int8 quantization in one pass over x.  The
+ * norm-then-quantize chain is the one the "MOSS-Image ... INT8" page
+ * describes: its file table, row "Changed", lists the RMSNorm weights that the
+ * SmoothQuant folding rewrote, and "How it was made" says those (1 + w)
+ * weights absorbed the activation smoothing, so the norm's output is exactly
+ * what the rotated linear quantizes.  Per row of x (fp32 arithmetic unless
+ * stated):
+ *    ms     = (float)(sum_k x[k]^2 / K)          (sum and quotient in fp64)
+ *    r      = 1 / sqrtf(ms + eps)                (IEEE divide and square root)
+ *    y[k]   = bf16_rne((x[k] * r) * (1 + norm_w[k]))
+ *    (xq, x_scale) = rotate_quant(y)             (as convrot_rotate_quant)
+ *   x       : bf16 bits [M, K]  (read)
+ *   norm_w  : fp32 [K]          (read; the stored weight w, applied as 1 + w;
+ *                                16-byte aligned like the tensors)
+ *   eps     : finite, >= 0; with eps == 0 an all-zero row has no defined
+ *             output (its y is NaN and its codes and scale are unspecified)
+ *   xq      : int8 [M, K]       (written)
+ *   x_scale : fp32 [M]          (written)
+ *   y_norm  : bf16 bits [M, K]  (written if not NULL: the normalised rows,
+ *             for a residual stream or a second consumer)
+ * The fp64 sum may be formed in any order; the codes and scale equal
+ * convrot_rotate_quant applied to y.
+ */
+int convrot_rmsnorm_rotate_quant(const uint16_t *x, const float *norm_w, float eps, int64_t M, int64_t K,
+                                 int group, int8_t *xq, float *x_scale, uint16_t *y_norm, hipStream_t stream);
 
 /*
  * convrot_workspace_size -- bytes of device workspace convrot_w8a8_linear and

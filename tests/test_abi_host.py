@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    for s in range(0, 8):
+    for s in range(0, 9):
         assert len(cr.convrot_status_string(s)) > 0
     assert "unknown" in cr.convrot_status_string(99)
     assert cr.convrot_version() >= 100
@@ -67,11 +67,15 @@ MIS = ctypes.c_void_p(0x10008)
 NUL = None
 S0 = ctypes.c_void_p(0)
 
-ERR = {"null": 1, "shape": 2, "group": 3, "align": 4, "ws": 5, "dtype": 7}
+ERR = {"null": 1, "shape": 2, "group": 3, "align": 4, "ws": 5, "dtype": 7, "arg": 8}
 
 
 def rq(x, M, K, g, q, s):
     return cr.load().convrot_rotate_quant(x, M, K, g, q, s, S0)
+
+
+def nrq(x, w, eps, M, K, g, q, s, y):
+    return cr.load().convrot_rmsnorm_rotate_quant(x, w, eps, M, K, g, q, s, y, S0)
 
 
 def lin8(x, M, K, w, ws, N, g, y, wsp, wsb):
@@ -104,6 +108,25 @@ def test_rotate_quant_validation(L):
     assert rq(A, 4, 256, 256, MIS, C) == ERR["align"]
     assert rq(A, 4, 256, 256, B, ctypes.c_void_p(0x30002)) == ERR["align"]
     assert rq(NUL, 0, 256, 256, NUL, NUL) == 0             # empty input: no-op
+
+
+def test_rmsnorm_rotate_quant_validation(L):
+    W4 = ctypes.c_void_p(0x60000)
+    assert nrq(NUL, W4, 1e-6, 4, 256, 256, B, C, D) == ERR["null"]
+    assert nrq(A, NUL, 1e-6, 4, 256, 256, B, C, D) == ERR["null"]
+    assert nrq(A, W4, 1e-6, 4, 256, 256, NUL, C, D) == ERR["null"]
+    assert nrq(A, W4, 1e-6, 4, 256, 256, B, NUL, D) == ERR["null"]
+    assert nrq(A, W4, -1e-6, 4, 256, 256, B, C, D) == ERR["arg"]
+    assert nrq(A, W4, float("nan"), 4, 256, 256, B, C, D) == ERR["arg"]
+    assert nrq(A, W4, float("inf"), 4, 256, 256, B, C, D) == ERR["arg"]
+    assert nrq(A, W4, 1e-6, 4, 300, 256, B, C, D) == ERR["shape"]
+    assert nrq(A, W4, 1e-6, 4, 272, 256, B, C, D) == ERR["shape"]
+    assert nrq(A, W4, 1e-6, -1, 256, 256, B, C, D) == ERR["shape"]
+    assert nrq(A, W4, 1e-6, 4, 256, 48, B, C, D) == ERR["group"]
+    assert nrq(A, ctypes.c_void_p(0x60004), 1e-6, 4, 256, 256, B, C, D) == ERR["align"]   # norm_w: 16 bytes
+    assert nrq(A, W4, 1e-6, 4, 256, 256, B, C, MIS) == ERR["align"]
+    assert nrq(MIS, W4, 1e-6, 4, 256, 256, B, C, NUL) == ERR["align"]
+    assert nrq(NUL, NUL, 1e-6, 0, 256, 256, NUL, NUL, NUL) == 0   # empty input: no-op
 
 
 def test_linear_validation(L):

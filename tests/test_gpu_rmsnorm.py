@@ -1,0 +1,124 @@
+"""GPU parity of the fused RMSNorm + rotate + quantize call against the oracle.
+
+The norm's bf16 output is compared bit for bit (same fp32 operation order,
+fp64 sum of squares); the codes and scales to the same bar as the plain
+rotate-quantize, and, on the GPU alone, the fused codes must equal those the
+plain call produces from the fused call's own bf16 output (the norm front end
+feeds the unchanged quantizer).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_helpers import (assert_codes_close, assert_scales_close, bf16_from_dev, bf16_to_dev, say,
+                               to_dev)
+from w8a8_quantized_linear_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+# (M, K, group): K a multiple of 1024 up to 16384 with group 256 takes the
+# register-resident fast kernel, the rest the generic one.
+CASES = [
+    (37, 1024, 256), (300, 2048, 256), (64, 3072, 256), (513, 4096, 256), (17, 6144, 256), (65, 8192, 256),
+    (9, 12288, 256), (5, 16384, 256),
+    (1, 16, 16), (40, 512, 256), (33, 4352, 256), (3, 32768, 256), (70, 4096, 16), (50, 2048, 1),
+    (21, 1152, 128), (64, 4096, 2),
+]
+
+
+def _inputs(M, K, seed):
+    n_out = max(1, K // 100)
+    x = wl.make_activations(M, K, n_out, seed=seed)
+    w = wl.make_norm_weight(K, n_out, seed=seed)
+    return x, w
+
+
+def _check_against_plain(lib, xq, xs, y, group):
+    """Fused codes/scales == plain rotate_quant of the fused bf16 output."""
+    xq2, xs2 = lib.rotate_quant(y, group=group)
+    assert np.array_equal(xq.cpu().numpy(), xq2.cpu().numpy())
+    assert np.array_equal(xs.cpu().numpy(), xs2.cpu().numpy())
+
+
+@pytest.mark.parametrize("M,K,g", CASES)
+def test_rmsnorm_rotate_quant_parity(lib, M, K, g):
+    say(f"rmsnorm_rotate_quant M={M} K={K} group={g}")
+    x, w = _inputs(M, K, seed=M * 11 + K + g)
+    eps = 1e-6
+    xq, xs, y = lib.rmsnorm_rotate_quant(bf16_to_dev(x), to_dev(w), eps=eps, group=g, want_y=True)
+    xq_ref, xs_ref, y_ref = oracle.rmsnorm_rotate_quant(x, w, eps=eps, group=g)
+    assert np.array_equal(bf16_from_dev(y), y_ref)
+    assert_scales_close(xs.cpu().numpy(), xs_ref)
+    assert_codes_close(xq.cpu().numpy(), xq_ref)
+    _check_against_plain(lib, xq, xs, y, g)
+    # Without the optional bf16 output the codes are the same.
+    xq3, xs3 = lib.rmsnorm_rotate_quant(bf16_to_dev(x), to_dev(w), eps=eps, group=g)
+    assert np.array_equal(xq3.cpu().numpy(), xq.cpu().numpy())
+    assert np.array_equal(xs3.cpu().numpy(), xs.cpu().numpy())
+
+
+@pytest.mark.parametrize("K", [4096, 4352])
+def test_rmsnorm_special_rows(lib, K):
+    """Rows with a closed-form norm: zero (stays zero), constant powers of two
+    (normalise to +-1 before the weights), one-hot (sqrt(K)), and rows of
+    extreme magnitude whose sum of squares leaves the fp32 range but not
+    fp64's."""
+    say(f"rmsnorm_rotate_quant special rows K={K}")
+    rng = np.random.default_rng(5)
+    x = np.zeros((8, K), dtype=np.float32)
+    x[1] = 4.0
+    x[2] = -0.125
+    x[3, 17] = 3.0
+    x[4] = rng.standard_normal(K) * 1e-30         # squares below fp32's range
+    x[5] = rng.standard_normal(K) * 1e18          # sum of squares above fp32's range
+    x[6, ::5] = -2.0
+    x[7] = rng.standard_normal(K)
+    xb = wl.float_to_bf16_bits(x)
+    w = wl.make_norm_weight(K, K // 100, seed=9)
+    xq, xs, y = lib.rmsnorm_rotate_quant(bf16_to_dev(xb), to_dev(w), eps=1e-6, want_y=True)
+    xq_ref, xs_ref, y_ref = oracle.rmsnorm_rotate_quant(xb, w, eps=1e-6)
+    yb = bf16_from_dev(y)
+    assert np.array_equal(yb, y_ref)
+    assert np.all(yb[0] == 0) and xs.cpu().numpy()[0] == 0 and np.all(xq.cpu().numpy()[0] == 0)
+    assert_scales_close(xs.cpu().numpy(), xs_ref)
+    assert_codes_close(xq.cpu().numpy(), xq_ref)
+    _check_against_plain(lib, xq, xs, y, 256)
+
+
+def test_rmsnorm_eps_zero_and_unit_weights(lib):
+    """eps = 0 and w = 0 on constant rows c = +-2^k: the norm is exactly +-1,
+    so every 256-column group rotates to +-16 in its first column and zeros
+    elsewhere, which quantizes to +-127 and 0 with scale 16/127."""
+    say("rmsnorm_rotate_quant eps=0, w=0")
+    K = 2048
+    x = np.empty((4, K), dtype=np.float32)
+    for i, c in enumerate((1.0, -8.0, 2.0 ** -20, 2.0 ** 30)):
+        x[i] = c
+    xb = wl.float_to_bf16_bits(x)
+    w = np.zeros(K, dtype=np.float32)
+    xq, xs, y = lib.rmsnorm_rotate_quant(bf16_to_dev(xb), to_dev(w), eps=0.0, want_y=True)
+    yf = wl.bf16_bits_to_float(bf16_from_dev(y))
+    assert np.all(yf == np.sign(x))
+    q = xq.cpu().numpy()
+    assert np.array_equal(q[:, ::256], np.repeat(127 * np.sign(x[:, :1]), K // 256, axis=1).astype(np.int8))
+    q[:, ::256] = 0
+    assert not q.any()
+    assert np.all(xs.cpu().numpy() == np.float32(16.0) / np.float32(127.0))
+    xq_ref, xs_ref, _ = oracle.rmsnorm_rotate_quant(xb, w, eps=0.0)
+    assert np.array_equal(xq.cpu().numpy(), xq_ref)
+    assert np.array_equal(xs.cpu().numpy(), xs_ref)
+
+
+def test_rmsnorm_stack_shape_sampled(lib):
+    """The decoder-stack norm input at full size (M = 8704 tokens, K = 4096):
+    the bf16 output in full, codes and scales on sampled tokens."""
+    M, K = 8704, 4096
+    say(f"rmsnorm_rotate_quant M={M} K={K}")
+    x, w = _inputs(M, K, seed=4)
+    xq, xs, y = lib.rmsnorm_rotate_quant(bf16_to_dev(x), to_dev(w), eps=1e-6, want_y=True)
+    assert np.array_equal(bf16_from_dev(y), oracle.rmsnorm(x, w, eps=1e-6))
+    rng = np.random.default_rng(8704)
+    toks = np.unique(np.concatenate([rng.choice(M, 256, replace=False), [0, M - 1]]))
+    xq_ref, xs_ref, _ = oracle.rmsnorm_rotate_quant(x[toks], w, eps=1e-6)
+    assert_scales_close(xs.cpu().numpy()[toks], xs_ref)
+    assert_codes_close(xq.cpu().numpy()[toks], xq_ref)

@@ -19,9 +19,9 @@ import os
 __all__ = [
     "load", "library_path", "ConvRotError",
     "convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
-    "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
+    "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
     "convrot_status_string", "convrot_version",
-    "quantize_weight", "rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8", "workspace",
+    "quantize_weight", "rotate_quant", "rmsnorm_rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8", "workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,11 +53,12 @@ def load():
             f"{_LIB_PATH} is not built; run `python -m w8a8_quantized_linear_amd.build` "
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(_LIB_PATH)
-    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    P, I64, I, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     sigs = {
         "convrot_quantize_weight": (I, [P, I, I64, I64, I, I, P, P, P]),
         "convrot_quantize_weight_i4_clip": (I, [P, I, I64, I64, I, P, P, P, P]),
         "convrot_rotate_quant": (I, [P, I64, I64, I, P, P, P]),
+        "convrot_rmsnorm_rotate_quant": (I, [P, P, F, I64, I64, I, P, P, P, P]),
         "convrot_workspace_size": (SZ, [I64, I64]),
         "convrot_w8a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
         "convrot_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
@@ -76,7 +77,7 @@ def load():
 def exported_symbols():
     """Names the binding expects the library to export."""
     return ["convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
-            "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
+            "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
             "convrot_status_string", "convrot_version"]
 
 
@@ -149,6 +150,11 @@ def convrot_rotate_quant(x, M, K, group, xq, x_scale, stream=None) -> int:
                                        _stream(stream))
 
 
+def convrot_rmsnorm_rotate_quant(x, norm_w, eps, M, K, group, xq, x_scale, y_norm=None, stream=None) -> int:
+    return load().convrot_rmsnorm_rotate_quant(_dptr(x), _dptr(norm_w), float(eps), int(M), int(K), int(group),
+                                               _dptr(xq), _dptr(x_scale), _dptr(y_norm), _stream(stream))
+
+
 def convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
     return load().convrot_w8a8_linear(_dptr(x), int(M), int(K), _dptr(wq), _dptr(w_scale), int(N), int(group),
                                       _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
@@ -201,6 +207,22 @@ def rotate_quant(x, group: int = 256):
     xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check("convrot_rotate_quant", convrot_rotate_quant(x, M, K, group, xq, xs))
     return xq, xs
+
+
+def rmsnorm_rotate_quant(x, norm_w, eps: float = 1e-6, group: int = 256, want_y: bool = False):
+    """RMSNorm with (1 + norm_w) weights fused with rotate_quant.
+    x bf16 [M, K], norm_w fp32 [K] -> (xq int8 [M, K], x_scale fp32 [M][, y bf16 [M, K]])."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    if norm_w.dtype != torch.float32:
+        raise TypeError("convrot.rmsnorm_rotate_quant: norm_w must be float32")
+    xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if want_y else None
+    _check("convrot_rmsnorm_rotate_quant",
+           convrot_rmsnorm_rotate_quant(x, norm_w, eps, M, K, group, xq, xs, y))
+    return (xq, xs, y) if want_y else (xq, xs)
 
 
 def workspace(M: int, K: int, device="cuda"):

@@ -37,7 +37,7 @@ constexpr int64_t kMaxRows = int64_t(1) << 30;
 
 extern "C" {
 
-int convrot_version(void) { return 100; }
+int convrot_version(void) { return 101; }
 
 const char* convrot_status_string(int status) {
   switch (status) {
@@ -51,6 +51,7 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_WORKSPACE: return "workspace smaller than convrot_workspace_size(M, K)";
     case CONVROT_ERR_DEVICE: return "the HIP runtime reported an error";
     case CONVROT_ERR_DTYPE: return "unsupported weight dtype or bit width";
+    case CONVROT_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0)";
     default: return "unknown convrot status";
   }
 }
@@ -101,6 +102,20 @@ int convrot_rotate_quant(const uint16_t* x, int64_t M, int64_t K, int group, int
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4)) return CONVROT_ERR_ALIGN;
   return device_status(
       convrot::launch_rotate_quant(x, CONVROT_W_BF16, M, K, log2_group(group), xq, x_scale, stream));
+}
+
+int convrot_rmsnorm_rotate_quant(const uint16_t* x, const float* norm_w, float eps, int64_t M, int64_t K,
+                                 int group, int8_t* xq, float* x_scale, uint16_t* y_norm, hipStream_t stream) {
+  if (int rc = check_k(K, group, false)) return rc;
+  if (M < 0) return CONVROT_ERR_SHAPE;
+  if (!(eps >= 0.0f) || !(eps <= 3.4028234663852886e38f)) return CONVROT_ERR_ARG;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !norm_w || !xq || !x_scale) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(x_scale, 4) || !aligned(norm_w, 16) ||
+      (y_norm && !aligned(y_norm, 16)))
+    return CONVROT_ERR_ALIGN;
+  return device_status(convrot::launch_rmsnorm_rotate_quant(x, norm_w, eps, M, K, log2_group(group), xq, x_scale,
+                                                            y_norm, stream));
 }
 
 int convrot_gemm_i8(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,

@@ -7,6 +7,14 @@
 
 namespace convrot {
 
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // x bf16 [rows, K] (in_dtype 1) or fp32 (in_dtype 0) -> codes int8 [rows, K]
 // with |code| <= qmax and fp32 scale [rows].  log2g = log2(group size).
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g,
@@ -17,6 +25,18 @@ hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_
 // without launching for other shapes.
 hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* x_scale,
                                     hipStream_t stream);
+
+// RMSNorm with (1 + w) weights, then the activation rotate-and-quantize of
+// its bf16 output (bf16 input only).  y_norm, if not null, receives the
+// normalised bf16 row.
+hipError_t launch_rmsnorm_rotate_quant(const uint16_t* x, const float* norm_w, float eps, int64_t rows, int64_t K,
+                                       int log2g, int8_t* codes, float* scale, uint16_t* y_norm,
+                                       hipStream_t stream);
+
+// Fast path of the above for group 256 (same shapes as launch_rotate_quant_g256).
+hipError_t launch_rmsnorm_rotate_quant_g256(const uint16_t* x, const float* norm_w, float eps, int64_t M,
+                                            int64_t K, int8_t* xq, float* x_scale, uint16_t* y_norm,
+                                            hipStream_t stream);
 
 // int4 weight preparation with the per-row clip search; clip_index may be null.
 hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,

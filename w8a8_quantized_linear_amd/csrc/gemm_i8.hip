@@ -69,13 +69,6 @@ constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 fa
 
 __device__ __forceinline__ int swz64(int r) { return ((r >> 2) ^ (r >> 3)) & 3; }
 
-// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
 
 // 4 packed bytes (8 nibbles, k = 0..7) -> 8 bytes of 16*q in natural k order.
 __device__ __forceinline__ void unpack4(uint32_t w, uint32_t& o0, uint32_t& o1) {

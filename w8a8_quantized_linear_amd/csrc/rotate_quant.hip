@@ -136,12 +136,15 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
          ((uint32_t(d) & 0xffu) << 24);
 }
 
-template <int TPT, int C, int IN, int MODE>
+template <int TPT, int C, int IN, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __restrict__ x, int64_t rows,
                                                                 int64_t K, int log2g, float inv_sqrt_g,
                                                                 float pow2_norm, void* __restrict__ codes,
                                                                 float* __restrict__ scale,
-                                                                int32_t* __restrict__ clip_index) {
+                                                                int32_t* __restrict__ clip_index,
+                                                                const float* __restrict__ norm_w, float eps,
+                                                                uint16_t* __restrict__ y_norm) {
+  static_assert(!NORM || (IN == IN_BF16 && MODE == MODE_I8), "the norm front end takes bf16 activations");
   constexpr int P = kThreads / TPT;  // rows per workgroup
   __shared__ float red_f[kWaves];
   __shared__ double red_d[kWaves];
@@ -162,6 +165,37 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __re
     } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[j][i] = 0.f;
+    }
+  }
+
+  if constexpr (NORM) {
+    // RMSNorm with (1 + w) weights; the rotation below sees its bf16 output.
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ss = __builtin_fma(double(v[j][i]), double(v[j][i]), ss);
+    ss = row_sum<TPT>(ss, red_d);
+    const float ms = float(ss / double(K));
+    const float r = 1.0f / sqrtf(ms + eps);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int64_t c = t + int64_t(TPT) * j;
+      if (c < nchunks) {
+        uint32_t yw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float w0 = norm_w[c * 16 + 2 * i], w1 = norm_w[c * 16 + 2 * i + 1];
+          yw[i] = pack_bf16x2((v[j][2 * i] * r) * (1.0f + w0), (v[j][2 * i + 1] * r) * (1.0f + w1));
+          v[j][2 * i] = __uint_as_float(yw[i] << 16);
+          v[j][2 * i + 1] = __uint_as_float(yw[i] & 0xffff0000u);
+        }
+        if (y_norm != nullptr && row_ok) {
+          uint4* dst = reinterpret_cast<uint4*>(y_norm + row * K + c * 16);
+          dst[0] = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+          dst[1] = make_uint4(yw[4], yw[5], yw[6], yw[7]);
+        }
+      }
     }
   }
 
@@ -255,9 +289,10 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __re
   }
 }
 
-template <int IN, int MODE>
+template <int IN, int MODE, bool NORM = false>
 hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* codes, float* scale,
-                    int32_t* clip_index, hipStream_t stream) {
+                    int32_t* clip_index, hipStream_t stream, const float* norm_w = nullptr, float eps = 0.f,
+                    uint16_t* y_norm = nullptr) {
   const int64_t nchunks = K / 16;
   const float inv_sqrt_g = float(1.0 / sqrt(double(1 << log2g)));
   const float pow2_norm = (log2g & 1) ? 1.0f : ldexpf(1.0f, -(log2g / 2));
@@ -271,8 +306,8 @@ hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* cod
   const int per_block = kThreads / tpt;
   const dim3 grid(unsigned((rows + per_block - 1) / per_block));
 #define CONVROT_RQ(TPT_, C_)                                                                          \
-  hipLaunchKernelGGL((rotate_quant_kernel<TPT_, C_, IN, MODE>), grid, dim3(kThreads), 0, stream, x, rows, K, \
-                     log2g, inv_sqrt_g, pow2_norm, codes, scale, clip_index)
+  hipLaunchKernelGGL((rotate_quant_kernel<TPT_, C_, IN, MODE, NORM>), grid, dim3(kThreads), 0, stream, x, rows, \
+                     K, log2g, inv_sqrt_g, pow2_norm, codes, scale, clip_index, norm_w, eps, y_norm)
   switch (tpt * 16 + c) {
     case 16 * 16 + 1: CONVROT_RQ(16, 1); break;
     case 32 * 16 + 1: CONVROT_RQ(32, 1); break;
@@ -303,6 +338,16 @@ hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_
   }
   if (in_dtype == IN_BF16) return dispatch<IN_BF16, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
   return dispatch<IN_F32, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
+}
+
+hipError_t launch_rmsnorm_rotate_quant(const uint16_t* x, const float* norm_w, float eps, int64_t rows, int64_t K,
+                                       int log2g, int8_t* codes, float* scale, uint16_t* y_norm,
+                                       hipStream_t stream) {
+  if (log2g == 8) {
+    const hipError_t e = launch_rmsnorm_rotate_quant_g256(x, norm_w, eps, rows, K, codes, scale, y_norm, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
+  return dispatch<IN_BF16, MODE_I8, true>(x, rows, K, log2g, codes, scale, nullptr, stream, norm_w, eps, y_norm);
 }
 
 hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,

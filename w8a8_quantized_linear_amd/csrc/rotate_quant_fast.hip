@@ -110,13 +110,16 @@ __device__ __forceinline__ int quantize(float n, float d, float r) {
   return int(q1 + half);  // v_cvt_i32_f32 truncates
 }
 
-template <int C, int TW>
+template <int C, int TW, bool NORM>
 __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                      int K, int8_t* __restrict__ xq,
-                                                                     float* __restrict__ x_scale) {
+                                                                     float* __restrict__ x_scale,
+                                                                     const float* __restrict__ norm_w, float eps,
+                                                                     uint16_t* __restrict__ y_norm) {
   static_assert(TW == 1 || TW == 2 || TW == 4, "waves per token");
   constexpr int P = kWaves / TW;  // tokens per workgroup iteration
   __shared__ float red[kWaves];
+  __shared__ double red_d[kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -149,24 +152,85 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
     }
   };
 
+  // RMSNorm: (1 + w) for this lane's columns, fixed across tokens.
+  float w1[NORM ? C : 1][16];
+  if constexpr (NORM) {
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *reinterpret_cast<const float4*>(norm_w + chunk_off(j) + 4 * q);
+        w1[j][4 * q + 0] = 1.0f + f.x;
+        w1[j][4 * q + 1] = 1.0f + f.y;
+        w1[j][4 * q + 2] = 1.0f + f.z;
+        w1[j][4 * q + 3] = 1.0f + f.w;
+      }
+  }
+
   int64_t grp = blockIdx.x;
   load(grp * P + wave / TW);
   for (; grp < ngroups; grp += gridDim.x) {
     const int64_t tok = grp * P + wave / TW;
+    uint32_t wd[C][8];  // the row's bf16 pairs as loaded (or as normalised)
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wd[j][i] = raw[j][0][i];
+        wd[j][4 + i] = raw[j][1][i];
+      }
+    // prefetch the next token of this wave while transforming this one
+    load((grp + gridDim.x) * P + wave / TW);
+
+    if constexpr (NORM) {
+      // mean square in fp64 (each square of a bf16 value is exact there),
+      // then y = bf16_rne((x * r) * (1 + w)) with r = 1 / sqrt(ms + eps)
+      double ss = 0.0;
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
+          ss = __builtin_fma(lo, lo, ss);
+          ss = __builtin_fma(hi, hi, ss);
+        }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+      if constexpr (TW > 1) {
+        if (lane == 0) red_d[wave] = ss;
+        __syncthreads();
+        const int first = (wave / TW) * TW;
+        ss = red_d[first];
+#pragma unroll
+        for (int w2 = 1; w2 < TW; ++w2) ss += red_d[first + w2];
+        __syncthreads();
+      }
+      const float ms = float(ss / double(K));
+      const float r = 1.0f / sqrtf(ms + eps);
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
+          wd[j][i] = pack_bf16x2((lo * r) * w1[j][2 * i], (hi * r) * w1[j][2 * i + 1]);
+        }
+        if (y_norm != nullptr && tok < M) {
+          u32x4* dst = reinterpret_cast<u32x4*>(y_norm + tok * K + chunk_off(j));
+          dst[0] = u32x4{wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
+          dst[1] = u32x4{wd[j][4], wd[j][5], wd[j][6], wd[j][7]};
+        }
+      }
+    }
+
     float v[C][16];
 #pragma unroll
-    for (int j = 0; j < C; ++j) {
-      const uint32_t w[8] = {raw[j][0][0], raw[j][0][1], raw[j][0][2], raw[j][0][3],
-                             raw[j][1][0], raw[j][1][1], raw[j][1][2], raw[j][1][3]};
+    for (int j = 0; j < C; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {  // unpack a bf16 pair and do the bit-0 butterfly
-        const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+        const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
         v[j][2 * i] = lo + hi;
         v[j][2 * i + 1] = lo - hi;
       }
-    }
-    // prefetch the next token of this wave while transforming this one
-    load((grp + gridDim.x) * P + wave / TW);
 
     float amax = 0.f;
 #pragma unroll
@@ -220,36 +284,50 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
   }
 }
 
-template <int C, int TW>
-hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, hipStream_t stream) {
+template <int C, int TW, bool NORM>
+hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w, float eps,
+                  uint16_t* y_norm, hipStream_t stream) {
   constexpr int P = kWaves / TW;
   const int64_t ngroups = (M + P - 1) / P;
   // enough workgroups to keep every CU busy with several waves each; the
   // rest is covered by the per-wave token loop
   const int64_t max_blocks = 256 * 8;
   const unsigned grid = unsigned(ngroups < max_blocks ? ngroups : max_blocks);
-  hipLaunchKernelGGL((rotate_quant_g256_kernel<C, TW>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K), xq, xs);
+  hipLaunchKernelGGL((rotate_quant_g256_kernel<C, TW, NORM>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K),
+                     xq, xs, norm_w, eps, y_norm);
   return hipGetLastError();
+}
+
+template <bool NORM>
+hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w, float eps,
+                    uint16_t* y_norm, hipStream_t stream) {
+  if (K % 1024 != 0) return hipErrorNotSupported;
+  switch (K / 1024) {
+    case 1: return launch<1, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 2: return launch<2, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 3: return launch<3, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 4: return launch<4, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 6: return launch<3, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 8: return launch<4, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 12: return launch<3, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    case 16: return launch<4, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    default: return hipErrorNotSupported;
+  }
 }
 
 }  // namespace
 
-// Returns hipErrorNotSupported (without launching) for shapes this path does
+// Return hipErrorNotSupported (without launching) for shapes this path does
 // not cover; the caller then uses the general kernel.
 hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                                     hipStream_t stream) {
-  if (K % 1024 != 0) return hipErrorNotSupported;
-  switch (K / 1024) {
-    case 1: return launch<1, 1>(x, M, K, xq, xs, stream);
-    case 2: return launch<2, 1>(x, M, K, xq, xs, stream);
-    case 3: return launch<3, 1>(x, M, K, xq, xs, stream);
-    case 4: return launch<4, 1>(x, M, K, xq, xs, stream);
-    case 6: return launch<3, 2>(x, M, K, xq, xs, stream);
-    case 8: return launch<4, 2>(x, M, K, xq, xs, stream);
-    case 12: return launch<3, 4>(x, M, K, xq, xs, stream);
-    case 16: return launch<4, 4>(x, M, K, xq, xs, stream);
-    default: return hipErrorNotSupported;
-  }
+  return launch_k<false>(x, M, K, xq, xs, nullptr, 0.f, nullptr, stream);
+}
+
+hipError_t launch_rmsnorm_rotate_quant_g256(const uint16_t* x, const float* norm_w, float eps, int64_t M,
+                                            int64_t K, int8_t* xq, float* xs, uint16_t* y_norm,
+                                            hipStream_t stream) {
+  return launch_k<true>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
 }
 
 }  // namespace convrot

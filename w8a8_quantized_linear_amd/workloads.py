@@ -104,6 +104,22 @@ def make_activations(M: int, K: int, n_outliers: int, seed: int) -> np.ndarray:
     return float_to_bf16_bits(x)
 
 
+NORM_W_STD = 0.25
+
+
+def make_norm_weight(K: int, n_outliers: int, seed: int) -> np.ndarray:
+    """fp32 [K] stored RMSNorm weights w (the norm applies 1 + w), as left by
+    a SmoothQuant fold: w ~ N(0, 0.25^2), and on the ``n_outliers`` outlier
+    channels of ``make_activations(.., seed)`` the factor 1 + w is divided by
+    sqrt(20) (the smoothing factor of a x20 channel at migration strength 0.5)."""
+    rng = np.random.default_rng([seed, 3])
+    w = rng.standard_normal(K, dtype=np.float32) * np.float32(NORM_W_STD)
+    if n_outliers:
+        ch = outlier_channels(K, n_outliers, seed)
+        w[ch] = (np.float32(1) + w[ch]) / np.float32(np.sqrt(OUTLIER_GAIN)) - np.float32(1)
+    return w.astype(np.float32)
+
+
 def make_weight(N: int, K: int, seed: int) -> np.ndarray:
     """fp32 [N, K] drawn from N(0, 0.02^2)."""
     rng = np.random.default_rng([seed, 2])
