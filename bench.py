@@ -11,11 +11,12 @@ step reads its operands from HBM.
 
 Prints ONE JSON line on stdout: TOPS (2*M*N*K per step / step time), plus
 tokens/s, the GEMM kernel's roofline position (timed live with HIP events on
-the launch stream), the rotate-quantize kernel's HBM bandwidth, and the CPU
-oracle timed on a bounded sample on this host.
+the launch stream), the rotate-quantize kernel's HBM bandwidth (also fused
+with the preceding RMSNorm), and the CPU oracle timed on a bounded sample on
+this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--profile {gemm,rq,rq_large,copy,linear}]
+                       [--no-extras] [--profile {gemm,rq,rq_large,rmsnorm_rq,copy,linear}]
 """
 from __future__ import annotations
 
@@ -56,6 +57,8 @@ RQ_SOURCES = ["w8a8_quantized_linear_amd/csrc/rotate_quant.hip",
 # 34 x 256-token stack's activations (K 4096 and the down projection's
 # K 12288) and the MLP down projection's input at M=2048.
 RQ_PASSES = [(8704, 4096), (8704, 12288), (2048, 12288)]
+# The stack's RMSNorm input (hidden size 4096), normalised and quantized in one pass.
+RMSNORM_PASS = (8704, 4096)
 
 
 def load_traffic(name, sources):
@@ -223,6 +226,37 @@ def rq_passes(torch, cr, timer):
     return res
 
 
+def rmsnorm_rq_pass(torch, cr, wl, timer):
+    """Fused RMSNorm + rotate-quantize on the decoder stack's norm input
+    (M=8704 tokens, K=4096), with and without the optional bf16 norm output,
+    beside the plain rotate-quantize of the same shape; buffer sets cycled
+    past 2x the MALL as in rq_passes."""
+    dev = torch.device("cuda")
+    m, k = RMSNORM_PASS
+    per = {"fused": m * (3 * k + 4) + 4 * k, "fused_y": m * (5 * k + 4) + 4 * k, "plain": m * (3 * k + 4)}
+    n = max(2, -(-2 * MALL_BYTES // per["fused_y"]) + 1)
+    g = torch.Generator(device=dev).manual_seed(m + k + 1)
+    xs = [torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
+    qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
+    ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
+    ys = [torch.empty((m, k), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    nw = torch.from_numpy(wl.make_norm_weight(k, k // 100, seed=4)).to(dev)
+    runs = {
+        "fused": lambda i: cr.convrot_rmsnorm_rotate_quant(xs[i % n], nw, 1e-6, m, k, GROUP, qs[i % n], ss[i % n]),
+        "fused_y": lambda i: cr.convrot_rmsnorm_rotate_quant(xs[i % n], nw, 1e-6, m, k, GROUP, qs[i % n],
+                                                             ss[i % n], ys[i % n]),
+        "plain": lambda i: cr.convrot_rotate_quant(xs[i % n], m, k, GROUP, qs[i % n], ss[i % n]),
+    }
+    res = {"M": m, "K": k, "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "traffic": load_traffic("rmsnorm_rotate_quant_M8704_K4096", RQ_SOURCES)}
+    for name, fn in runs.items():
+        t = timer.time(fn, 60, warm=5)
+        res[name] = {"us": round(t * 1e6, 2), "bytes": per[name], "achieved": round(per[name] / t / 1e9, 1),
+                     "frac": round(per[name] / t / 1e9 / PEAK_HBM_GBS, 4)}
+    del xs, qs, ss, ys
+    return res
+
+
 def copy_peak(torch, timer):
     """Measured device-to-device copy bandwidth (1 GiB, read + write bytes)."""
     a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
@@ -254,6 +288,17 @@ def profile_mode(mode, torch, cr, wl):
         torch.cuda.synchronize()
         log(f"profile mode rq_large M={m} K={k}: 3 launches")
         return
+    if mode == "rmsnorm_rq":
+        m, k = RMSNORM_PASS
+        xd = torch.randn((m, k), device=dev).to(torch.bfloat16)
+        nw = torch.from_numpy(wl.make_norm_weight(k, k // 100, seed=4)).to(dev)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xs = torch.empty((m,), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            cr.convrot_rmsnorm_rotate_quant(xd, nw, 1e-6, m, k, GROUP, xq, xs)
+        torch.cuda.synchronize()
+        log(f"profile mode rmsnorm_rq M={m} K={k}: 3 launches")
+        return
     x, w, sets = build_sets(torch, cr, wl, 1)
     xd, wq, ws, y, wsp = sets[0]
     xq, xs = cr.rotate_quant(xd)
@@ -275,7 +320,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "rq", "rq_large", "copy", "linear"], default=None)
+    ap.add_argument("--profile", choices=["gemm", "rq", "rq_large", "rmsnorm_rq", "copy", "linear"], default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -389,6 +434,8 @@ def main():
                                  "passes": rq_passes(torch, cr, timer),
                                  "traffic": load_traffic("rotate_quant_M8704_K12288", RQ_SOURCES),
                                  "copy_peak_measured": copy_peak(torch, timer)}
+    log("fused RMSNorm + rotate-quantize M=8704 K=4096")
+    out["rmsnorm_rotate_quant"] = rmsnorm_rq_pass(torch, cr, wl, timer)
     if not args.no_extras:
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)

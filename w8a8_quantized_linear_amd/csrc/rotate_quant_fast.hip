@@ -152,18 +152,37 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
     }
   };
 
-  // RMSNorm: (1 + w) for this lane's columns, fixed across tokens.
-  float w1[NORM ? C : 1][16];
-  if constexpr (NORM) {
+  // RMSNorm: the factors 1 + w of the columns a lane owns are fixed across
+  // tokens.  Up to 48 KB they are kept in LDS, where they cost no
+  // occupancy: entry ((j * TW + t) * 4 + q) * 64 + l holds columns
+  // [4q, 4q + 4) of chunk j of lane l of the token's wave t, so a wave's
+  // 16-byte reads are consecutive.  The workgroup fills it together.
+  // Larger rows (K = 16384) keep them in registers, as LDS would then
+  // limit occupancy more than registers do.
+  constexpr bool kW1Lds = NORM && C * TW * 4096 <= 49152;
+  __shared__ float4 w1s[kW1Lds ? C * TW * 4 * 64 : 1];
+  float w1r[NORM && !kW1Lds ? C : 1][16];
+  if constexpr (kW1Lds) {
+#pragma unroll
+    for (int k = 0; k < C * TW; ++k) {
+      const int e = k * kThreads + threadIdx.x;  // < C * TW * 256
+      const int l = e & 63, q = (e >> 6) & 3, jt = e >> 8;
+      const int lg = l & 15, lu = lg ^ ((lg & 4) ? 3 : 0);
+      const int col = ((jt / TW) * (64 * TW) + (jt % TW) * 64 + (l & ~15) + lu) * 16 + 4 * q;
+      const float4 f = *reinterpret_cast<const float4*>(norm_w + col);
+      w1s[e] = make_float4(1.0f + f.x, 1.0f + f.y, 1.0f + f.z, 1.0f + f.w);
+    }
+    __syncthreads();
+  } else if constexpr (NORM) {
 #pragma unroll
     for (int j = 0; j < C; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 f = *reinterpret_cast<const float4*>(norm_w + chunk_off(j) + 4 * q);
-        w1[j][4 * q + 0] = 1.0f + f.x;
-        w1[j][4 * q + 1] = 1.0f + f.y;
-        w1[j][4 * q + 2] = 1.0f + f.z;
-        w1[j][4 * q + 3] = 1.0f + f.w;
+        w1r[j][4 * q + 0] = 1.0f + f.x;
+        w1r[j][4 * q + 1] = 1.0f + f.y;
+        w1r[j][4 * q + 2] = 1.0f + f.z;
+        w1r[j][4 * q + 3] = 1.0f + f.w;
       }
   }
 
@@ -210,9 +229,21 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
 #pragma unroll
       for (int j = 0; j < C; ++j) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
-          wd[j][i] = pack_bf16x2((lo * r) * w1[j][2 * i], (hi * r) * w1[j][2 * i + 1]);
+        for (int q = 0; q < 4; ++q) {
+          float w1[4];
+          if constexpr (kW1Lds) {
+            const float4 f = w1s[((j * TW + wt) * 4 + q) * 64 + lane];
+            w1[0] = f.x, w1[1] = f.y, w1[2] = f.z, w1[3] = f.w;
+          } else {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) w1[h] = w1r[j][4 * q + h];
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int i = 2 * q + h;
+            const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
+            wd[j][i] = pack_bf16x2((lo * r) * w1[2 * h], (hi * r) * w1[2 * h + 1]);
+          }
         }
         if (y_norm != nullptr && tok < M) {
           u32x4* dst = reinterpret_cast<u32x4*>(y_norm + tok * K + chunk_off(j));
