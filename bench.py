@@ -174,9 +174,20 @@ def extras_w4a8(torch, cr, wl, timer):
             "tokens_per_s": cfg.M / t, "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
 
 
+def _ok(cr, rc):
+    if rc != 0:
+        raise RuntimeError(f"convrot status {rc}: {cr.convrot_status_string(rc)}")
+
+
 def extras_stack(torch, cr, wl, timer):
-    """32-layer synthetic decoder linear stack at M=8704: 224 linear calls per
-    pass (each with its own rotate-quantize), weights generated on device."""
+    """32-layer synthetic decoder linear stack at M=8704, weights generated on
+    device.  Three ways of running each layer's seven linears:
+    - per linear: 7 rotate-quantize passes and 7 GEMM launches;
+    - shared input: q/k/v and gate/up each share one rotate-quantize and one
+      multi-output GEMM launch (4 passes, 4 launches);
+    - shared input with the RMSNorm fused: as above, with the norms in front
+      of q/k/v and gate/up folded into their rotate-quantize passes (so this
+      variant does the two norms' work too)."""
     cfg = wl.CONFIGS["C4"]
     dev = torch.device("cuda")
     acts = [torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16) for a in wl.stack_activations()]
@@ -188,23 +199,51 @@ def extras_stack(torch, cr, wl, timer):
             ws_.append(cr.quantize_weight(wd))
             del wd
         layers.append(ws_)
-    outs = {n: torch.empty((cfg.M, n), dtype=torch.bfloat16, device=dev) for n in {l.N for l in cfg.linears}}
+    outs = {lin.name: torch.empty((cfg.M, lin.N), dtype=torch.bfloat16, device=dev) for lin in cfg.linears}
     wsp = cr.workspace(cfg.M, 12288, dev)
+    nws = [torch.from_numpy(wl.make_norm_weight(4096, 41, seed=s)).to(dev) for s in (4, 6)]
+    xq = torch.empty((cfg.M, 4096), dtype=torch.int8, device=dev)
+    xs = torch.empty((cfg.M,), dtype=torch.float32, device=dev)
     ops = 0.0
     for lin in cfg.linears:
         ops += 2.0 * cfg.M * lin.N * lin.K
     ops *= cfg.layers
+    names = [lin.name for lin in cfg.linears]
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
-    def one_pass(_):
+    def per_linear(_):
         for layer in range(cfg.layers):
             for li, lin in enumerate(cfg.linears):
                 wq, wsc = layers[layer][li]
-                cr.w8a8_linear(acts[wl.C4_INPUT_OF[lin.name]], wq, wsc, out=outs[lin.N], ws=wsp)
+                cr.w8a8_linear(acts[wl.C4_INPUT_OF[lin.name]], wq, wsc, out=outs[lin.name], ws=wsp)
 
-    t = timer.time(one_pass, 3, warm=1)
-    return {"workload": "32-layer linear stack, M=8704 (34 x 256 tokens), 224 W8A8 linears",
-            "ms_per_pass": t * 1e3, "tokens_per_s": cfg.M / t, "tops": ops / t / 1e12,
-            "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
+    def shared(_):
+        for layer in range(cfg.layers):
+            for gi, grp in enumerate(groups):
+                cr.linear_multi(acts[gi], [layers[layer][names.index(n)] for n in grp],
+                                outs=[outs[n] for n in grp], ws=wsp)
+
+    def fused_norm(_):
+        for layer in range(cfg.layers):
+            for gi, grp in enumerate(groups):
+                a = acts[gi]
+                M, K = a.shape
+                if gi in (0, 2):
+                    _ok(cr, cr.convrot_rmsnorm_rotate_quant(a, nws[gi // 2], 1e-6, M, K, GROUP, xq, xs))
+                    desc = [(layers[layer][names.index(n)][0], layers[layer][names.index(n)][1],
+                             outs[n].shape[1], None, outs[n]) for n in grp]
+                    _ok(cr, cr.convrot_gemm_i8_multi(xq, xs, 8, M, K, desc))
+                else:
+                    wq, wsc = layers[layer][names.index(grp[0])]
+                    cr.w8a8_linear(a, wq, wsc, out=outs[grp[0]], ws=wsp)
+
+    res = {"workload": "32-layer linear stack, M=8704 (34 x 256 tokens), 224 W8A8 linears"}
+    for key, fn in (("per_linear", per_linear), ("shared_input", shared), ("shared_input_fused_norm", fused_norm)):
+        t = timer.time(fn, 3, warm=1)
+        res[key] = {"ms_per_pass": t * 1e3, "tokens_per_s": cfg.M / t, "tops": ops / t / 1e12,
+                    "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
+    res.update(res["per_linear"])
+    return res
 
 
 def rq_passes(torch, cr, timer):

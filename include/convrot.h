@@ -41,7 +41,8 @@
  *  - Tensor pointers must be 16-byte aligned; scale pointers 4-byte aligned.
  *  - Shapes: K % 16 == 0, K % group == 0, K <= CONVROT_MAX_K; int4 weights
  *    additionally need K % 32 == 0.  The calls that multiply (the linears
- *    and convrot_gemm_i8) accept M, N <= 2^30.  group must be a power of two in
+ *    and the GEMMs) accept M, N <= 2^30 with ceil(M/128) * ceil(N/128) < 2^31
+ *    (summed over the outputs of a multi-output call).  group must be a power of two in
  *    [1, 256]; group 1 means no rotation (plain row-wise int8).  Unlike the
  *    converter described on "qwen3vl_8b_int8_convrot" ("Layer and group
  *    selection"), the library never silently falls back to group 1 when K is
@@ -71,7 +72,8 @@ enum convrot_status {
   CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than convrot_workspace_size() */
   CONVROT_ERR_DEVICE = 6,    /* the HIP runtime reported an error while enqueueing */
   CONVROT_ERR_DTYPE = 7,     /* unsupported w_dtype or bits value */
-  CONVROT_ERR_ARG = 8        /* a scalar argument is out of range (eps negative, NaN or infinite) */
+  CONVROT_ERR_ARG = 8        /* a scalar argument is out of range (eps negative, NaN or infinite;
+                                n_outs outside [1, CONVROT_MAX_OUTS]) */
 };
 
 /* Weight dtypes accepted by convrot_quantize_weight. */
@@ -192,6 +194,50 @@ int convrot_gemm_i8(const int8_t *xq, const float *x_scale, const void *wq, int 
  */
 int convrot_quantize_weight_i4_clip(const void *w, int w_dtype, int64_t N, int64_t K, int group, uint8_t *wq4,
                                     float *w_scale, int32_t *clip_index, hipStream_t stream);
+
+/*
+ * Several linears that read the same input: the q, k and v projections of an
+ * attention block, or the gate and up projections of an MLP (the per-layer
+ * projection list of "craftingmod/Qwen3-VL-8B-Heretic-INT8", "Quantization
+ * metadata", names them; each is its own ConvRot int8 matrix as in
+ * "MOSS-Image ... INT8", file table row "Quantized").  The input is rotated
+ * and quantized once, and one GEMM launch computes every output: the column
+ * tiles of all weight matrices form one grid, so small projections (k, v)
+ * no longer leave compute units idle.  Each output is exactly what the
+ * single-output call gives for the same weight.
+ */
+#define CONVROT_MAX_OUTS 8
+
+/* One weight matrix of a multi-output call and where its results go. */
+typedef struct convrot_linear_out {
+  const void *wq;        /* int8 [N, K] (wbits 8) or uint8 [N, K/2] (wbits 4), 16-byte aligned */
+  const float *w_scale;  /* fp32 [N]; may be NULL when y is NULL */
+  int64_t N;             /* rows of wq, in (0, 2^30] */
+  int32_t *acc_out;      /* int32 [M, N] accumulators, or NULL */
+  uint16_t *y;           /* bf16 bits [M, N], or NULL */
+} convrot_linear_out;
+
+/*
+ * convrot_gemm_i8_multi -- convrot_gemm_i8 for n_outs (1..CONVROT_MAX_OUTS)
+ * weight matrices sharing xq [M, K] and x_scale [M], all of bit width wbits.
+ * Every output must ask for the same results: y in all of them or in none,
+ * likewise acc_out (CONVROT_ERR_NULL otherwise), and at least one of the
+ * two.  outs is a HOST array, read before the call returns.
+ */
+int convrot_gemm_i8_multi(const int8_t *xq, const float *x_scale, int wbits, int64_t M, int64_t K,
+                          const convrot_linear_out *outs, int n_outs, hipStream_t stream);
+
+/*
+ * convrot_linear_multi -- rotate + quantize x [M, K] once (as
+ * convrot_rotate_quant) into the workspace, then convrot_gemm_i8_multi with
+ * the bf16 epilogue: y_o = bf16(((xq . wq_o^T) * x_scale) * w_scale_o) for
+ * every output o.  wbits 8 (W8A8) or 4 (W4A8, K % 32 == 0).  Every output
+ * needs y and w_scale; acc_out must be NULL in all of them or set in all.
+ * workspace: at least convrot_workspace_size(M, K) bytes, 16-byte aligned.
+ */
+int convrot_linear_multi(const uint16_t *x, int64_t M, int64_t K, int group, int wbits,
+                         const convrot_linear_out *outs, int n_outs, void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *convrot_status_string(int status);

@@ -165,3 +165,56 @@ def test_gemm_validation(L):
     big = (1 << 30) + 1                                              # 32-bit tile indexing bound
     assert gemm(A, B, C, 8, D, big, 4, 64, E, NUL) == ERR["shape"]
     assert gemm(A, B, C, 8, D, 4, big, 64, E, NUL) == ERR["shape"]
+
+
+def outs_arr(*rows):
+    arr = (cr.LinearOut * len(rows))()
+    for i, r in enumerate(rows):
+        arr[i] = cr.LinearOut(*r)
+    return arr
+
+
+def gm(xq, xs, wb, M, K, outs, n=None):
+    return cr.load().convrot_gemm_i8_multi(xq, xs, wb, M, K, outs, len(outs) if n is None else n, S0)
+
+
+def lm(x, M, K, g, wb, outs, wsp, wsb, n=None):
+    return cr.load().convrot_linear_multi(x, M, K, g, wb, outs, len(outs) if n is None else n, wsp, wsb, S0)
+
+
+def test_multi_validation(L):
+    ok = (0x100000, 0x200000, 512, 0x300000, 0x400000)       # wq, w_scale, N, acc_out, y
+    ok_y = (0x500000, 0x600000, 128, None, 0x700000)
+    assert gm(A, B, 8, 4, 64, outs_arr(ok), n=0) == ERR["arg"]
+    assert gm(A, B, 8, 4, 64, outs_arr(*[ok] * 9)) == ERR["arg"]
+    assert gm(A, B, 3, 4, 64, outs_arr(ok)) == ERR["dtype"]
+    assert gm(A, B, 8, 4, 48 + 1, outs_arr(ok)) == ERR["shape"]
+    assert gm(A, B, 4, 4, 48, outs_arr(ok)) == ERR["shape"]          # int4 needs K % 32
+    assert gm(A, B, 8, 4, 64, outs_arr(ok, (0x100000, 0x200000, 0, 0x300000, 0x400000))) == ERR["shape"]
+    assert gm(A, B, 8, 4, 64, outs_arr(ok, (0x100000, 0x200000, (1 << 30) + 1, 0x300000, 0x400000))) == ERR["shape"]
+    assert gm(A, B, 8, 4, 64, outs_arr(ok, ok_y)) == ERR["null"]     # acc_out in one output only
+    assert gm(A, B, 8, 4, 64, outs_arr((0x100000, 0x200000, 64, None, None))) == ERR["null"]
+    assert gm(A, B, 8, 4, 64, outs_arr((0x100000, None, 64, 0x300000, 0x400000))) == ERR["null"]  # y needs w_scale
+    assert gm(A, NUL, 8, 4, 64, outs_arr(ok)) == ERR["null"]         # y needs x_scale
+    assert gm(A, B, 8, 4, 64, outs_arr((0x100008, 0x200000, 64, 0x300000, 0x400000))) == ERR["align"]
+    assert gm(A, B, 8, 4, 64, outs_arr((0x100000, 0x200002, 64, 0x300000, 0x400000))) == ERR["align"]
+    assert gm(MIS, B, 8, 4, 64, outs_arr(ok)) == ERR["align"]
+    assert gm(NUL, NUL, 8, 0, 64, outs_arr(ok)) == 0                   # empty input: no-op
+    assert cr.load().convrot_gemm_i8_multi(A, B, 8, 4, 64, None, 1, S0) == ERR["null"]
+    # 128-row tiles of all outputs must stay below 2^31
+    big = (0x100000, 0x200000, 1 << 30, 0x300000, 0x400000)
+    assert gm(A, B, 8, 1 << 30, 64, outs_arr(big)) == ERR["shape"]
+    need = cr.convrot_workspace_size(8, 512)
+    assert lm(A, 8, 512, 256, 8, outs_arr(ok_y), E, need - 1) == ERR["ws"]
+    assert lm(A, 8, 512, 256, 8, outs_arr((0x100000, 0x200000, 64, 0x300000, None)), E, need) == ERR["null"]
+    assert lm(A, 8, 512, 100, 8, outs_arr(ok_y), E, need) == ERR["group"]
+    assert lm(A, 8, 528, 16, 4, outs_arr(ok_y), E, need) == ERR["shape"]
+    assert lm(A, 8, 512, 256, 5, outs_arr(ok_y), E, need) == ERR["dtype"]
+    assert lm(NUL, 8, 512, 256, 8, outs_arr(ok_y), E, need) == ERR["null"]
+    assert lm(A, 8, 512, 256, 8, outs_arr(ok_y), MIS, need) == ERR["align"]
+    assert lm(NUL, 0, 512, 256, 8, outs_arr(ok_y), NUL, 0) == 0
+
+
+def test_single_gemm_tile_count_bound(L):
+    """M and N each within 2^30 but too many 128 x 128 tiles together."""
+    assert gemm(A, B, C, 8, D, 1 << 30, 1 << 20, 64, E, NUL) == ERR["shape"]

@@ -17,11 +17,12 @@ import ctypes
 import os
 
 __all__ = [
-    "load", "library_path", "ConvRotError",
+    "load", "library_path", "ConvRotError", "LinearOut", "MAX_OUTS",
     "convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
-    "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
-    "convrot_status_string", "convrot_version",
-    "quantize_weight", "rotate_quant", "rmsnorm_rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8", "workspace",
+    "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear",
+    "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi", "convrot_status_string", "convrot_version",
+    "quantize_weight", "rotate_quant", "rmsnorm_rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8",
+    "gemm_i8_multi", "linear_multi", "workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,13 @@ _lib = None
 OK = 0
 W_F32, W_BF16 = 0, 1
 MAX_K = 32768
+MAX_OUTS = 8
+
+
+class LinearOut(ctypes.Structure):
+    """convrot_linear_out: one weight matrix of a multi-output call."""
+    _fields_ = [("wq", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("acc_out", ctypes.c_void_p), ("y", ctypes.c_void_p)]
 
 
 class ConvRotError(RuntimeError):
@@ -63,6 +71,8 @@ def load():
         "convrot_w8a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
         "convrot_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P, P, SZ, P]),
         "convrot_gemm_i8": (I, [P, P, P, I, P, I64, I64, I64, P, P, P]),
+        "convrot_gemm_i8_multi": (I, [P, P, I, I64, I64, P, I, P]),
+        "convrot_linear_multi": (I, [P, I64, I64, I, I, P, I, P, SZ, P]),
         "convrot_status_string": (ctypes.c_char_p, [I]),
         "convrot_version": (I, []),
     }
@@ -77,7 +87,8 @@ def load():
 def exported_symbols():
     """Names the binding expects the library to export."""
     return ["convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
-            "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear", "convrot_gemm_i8",
+            "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear",
+            "convrot_w4a8_linear", "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi",
             "convrot_status_string", "convrot_version"]
 
 
@@ -170,6 +181,27 @@ def convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc_out, y, stream
                                   int(N), int(K), _dptr(acc_out), _dptr(y), _stream(stream))
 
 
+def _outs_array(outs):
+    """Sequence of (wq, w_scale, N, acc_out, y) (tensors or None, and N) ->
+    ctypes array of LinearOut."""
+    arr = (LinearOut * max(1, len(outs)))()
+    for i, (wq, ws, n, acc, y) in enumerate(outs):
+        arr[i] = LinearOut(_dptr(wq), _dptr(ws), int(n), _dptr(acc), _dptr(y))
+    return arr
+
+
+def convrot_gemm_i8_multi(xq, x_scale, wbits, M, K, outs, stream=None) -> int:
+    """outs: sequence of (wq, w_scale, N, acc_out, y)."""
+    return load().convrot_gemm_i8_multi(_dptr(xq), _dptr(x_scale), int(wbits), int(M), int(K),
+                                        _outs_array(outs), len(outs), _stream(stream))
+
+
+def convrot_linear_multi(x, M, K, group, wbits, outs, workspace, workspace_bytes, stream=None) -> int:
+    """outs: sequence of (wq, w_scale, N, acc_out, y)."""
+    return load().convrot_linear_multi(_dptr(x), int(M), int(K), int(group), int(wbits), _outs_array(outs),
+                                       len(outs), _dptr(workspace), int(workspace_bytes), _stream(stream))
+
+
 # ----------------------------------------------------- allocating helpers
 
 def quantize_weight(w, group: int = 256, bits: int = 8, with_clip_index: bool = False):
@@ -223,6 +255,38 @@ def rmsnorm_rotate_quant(x, norm_w, eps: float = 1e-6, group: int = 256, want_y:
     _check("convrot_rmsnorm_rotate_quant",
            convrot_rmsnorm_rotate_quant(x, norm_w, eps, M, K, group, xq, xs, y))
     return (xq, xs, y) if want_y else (xq, xs)
+
+
+def linear_multi(x, weights, wbits: int = 8, group: int = 256, outs=None, ws=None):
+    """Several linears on one input (rotated and quantized once, one GEMM
+    launch).  weights: sequence of (wq, w_scale); returns the list of bf16
+    outputs [M, N_o] (or fills ``outs``)."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    if outs is None:
+        outs = [torch.empty((M, wq.shape[0]), dtype=torch.bfloat16, device=x.device) for wq, _ in weights]
+    if ws is None:
+        ws = workspace(M, K, x.device)
+    desc = [(wq, wsc, wq.shape[0], None, y) for (wq, wsc), y in zip(weights, outs)]
+    _check("convrot_linear_multi", convrot_linear_multi(x, M, K, group, wbits, desc, ws, ws.numel()))
+    return outs
+
+
+def gemm_i8_multi(xq, x_scale, weights, wbits: int = 8, want_acc: bool = True, want_y: bool = True):
+    """convrot_gemm_i8 over several weight matrices sharing xq; returns a list
+    of (acc int32 [M, N_o] or None, y bf16 [M, N_o] or None)."""
+    torch = _torch()
+    M, K = xq.shape
+    res, desc = [], []
+    for wq, wsc in weights:
+        n = wq.shape[0]
+        acc = torch.empty((M, n), dtype=torch.int32, device=xq.device) if want_acc else None
+        y = torch.empty((M, n), dtype=torch.bfloat16, device=xq.device) if want_y else None
+        res.append((acc, y))
+        desc.append((wq, wsc, n, acc, y))
+    _check("convrot_gemm_i8_multi", convrot_gemm_i8_multi(xq, x_scale, wbits, M, K, desc))
+    return res
 
 
 def workspace(M: int, K: int, device="cuda"):

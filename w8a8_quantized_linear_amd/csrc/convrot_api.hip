@@ -33,11 +33,51 @@ int device_status(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_
 // The GEMM indexes tiles, rows and columns with 32-bit integers.
 constexpr int64_t kMaxRows = int64_t(1) << 30;
 
+// Output tiles of the smallest tile shape (128 x 128) must count below 2^31.
+bool tiles_fit(int64_t M, int64_t col_tiles) { return ((M + 127) / 128) * col_tiles < (int64_t(1) << 31); }
+
+// Checks shared by the multi-output calls (shapes, then pointers, then
+// alignment; the pointer checks are skipped for M == 0).
+int check_outs(int64_t M, const convrot_linear_out* outs, int n_outs, bool linear) {
+  if (n_outs < 1 || n_outs > CONVROT_MAX_OUTS) return CONVROT_ERR_ARG;
+  if (!outs) return CONVROT_ERR_NULL;
+  int64_t col_tiles = 0;
+  for (int o = 0; o < n_outs; ++o) {
+    if (outs[o].N <= 0 || outs[o].N > kMaxRows) return CONVROT_ERR_SHAPE;
+    col_tiles += (outs[o].N + 127) / 128;
+  }
+  if (!tiles_fit(M, col_tiles)) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  const bool has_y = outs[0].y != nullptr, has_acc = outs[0].acc_out != nullptr;
+  if (linear && !has_y) return CONVROT_ERR_NULL;
+  if (!has_y && !has_acc) return CONVROT_ERR_NULL;
+  for (int o = 0; o < n_outs; ++o) {
+    const convrot_linear_out& d = outs[o];
+    if (!d.wq || (d.y != nullptr) != has_y || (d.acc_out != nullptr) != has_acc) return CONVROT_ERR_NULL;
+    if (has_y && !d.w_scale) return CONVROT_ERR_NULL;
+  }
+  for (int o = 0; o < n_outs; ++o) {
+    const convrot_linear_out& d = outs[o];
+    if (!aligned(d.wq, 16) || (d.y && !aligned(d.y, 16)) || (d.acc_out && !aligned(d.acc_out, 16)) ||
+        (d.w_scale && !aligned(d.w_scale, 4)))
+      return CONVROT_ERR_ALIGN;
+  }
+  return CONVROT_OK;
+}
+
+hipError_t launch_outs(const int8_t* xq, const float* xs, int wbits, int64_t M, int64_t K,
+                       const convrot_linear_out* outs, int n_outs, hipStream_t stream) {
+  convrot::GemmOutDesc d[CONVROT_MAX_OUTS];
+  for (int o = 0; o < n_outs; ++o)
+    d[o] = {outs[o].wq, outs[o].w_scale, int(outs[o].N), int(outs[o].N), outs[o].acc_out, outs[o].y};
+  return convrot::launch_gemm_multi(xq, xs, wbits, M, K, d, n_outs, stream);
+}
+
 }  // namespace
 
 extern "C" {
 
-int convrot_version(void) { return 101; }
+int convrot_version(void) { return 102; }
 
 const char* convrot_status_string(int status) {
   switch (status) {
@@ -51,7 +91,8 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_WORKSPACE: return "workspace smaller than convrot_workspace_size(M, K)";
     case CONVROT_ERR_DEVICE: return "the HIP runtime reported an error";
     case CONVROT_ERR_DTYPE: return "unsupported weight dtype or bit width";
-    case CONVROT_ERR_ARG: return "a scalar argument is out of range (eps must be finite and >= 0)";
+    case CONVROT_ERR_ARG: return "a scalar argument is out of range (eps negative or not finite, or n_outs "
+                                 "outside [1, 8])";
     default: return "unknown convrot status";
   }
 }
@@ -123,7 +164,7 @@ int convrot_gemm_i8(const int8_t* xq, const float* x_scale, const void* wq, int 
   if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
   if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || K > CONVROT_MAX_K || (wbits == 4 && K % 32 != 0))
     return CONVROT_ERR_SHAPE;
-  if (M > kMaxRows || N > kMaxRows) return CONVROT_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || !tiles_fit(M, (N + 127) / 128)) return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!xq || !wq || (!acc_out && !y)) return CONVROT_ERR_NULL;
   if (y && (!x_scale || !w_scale)) return CONVROT_ERR_NULL;
@@ -137,7 +178,8 @@ static int linear_impl(const uint16_t* x, int64_t M, int64_t K, const void* wq, 
                        int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
   if (int rc = check_k(K, group, wbits == 4)) return rc;
-  if (M < 0 || N <= 0 || M > kMaxRows || N > kMaxRows) return CONVROT_ERR_SHAPE;
+  if (M < 0 || N <= 0 || M > kMaxRows || N > kMaxRows || !tiles_fit(M, (N + 127) / 128))
+    return CONVROT_ERR_SHAPE;
   if (M == 0) return CONVROT_OK;
   if (!x || !wq || !w_scale || !y || !workspace) return CONVROT_ERR_NULL;
   if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
@@ -160,6 +202,37 @@ int convrot_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   return linear_impl(x, M, K, wq4, 4, w_scale, N, group, y, workspace, workspace_bytes, stream);
+}
+
+int convrot_gemm_i8_multi(const int8_t* xq, const float* x_scale, int wbits, int64_t M, int64_t K,
+                          const convrot_linear_out* outs, int n_outs, hipStream_t stream) {
+  if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
+  if (M < 0 || M > kMaxRows || K <= 0 || K % 16 != 0 || K > CONVROT_MAX_K || (wbits == 4 && K % 32 != 0))
+    return CONVROT_ERR_SHAPE;
+  if (int rc = check_outs(M, outs, n_outs, false)) return rc;
+  if (M == 0) return CONVROT_OK;
+  if (!xq) return CONVROT_ERR_NULL;
+  if (outs[0].y && !x_scale) return CONVROT_ERR_NULL;
+  if (!aligned(xq, 16) || (x_scale && !aligned(x_scale, 4))) return CONVROT_ERR_ALIGN;
+  return device_status(launch_outs(xq, x_scale, wbits, M, K, outs, n_outs, stream));
+}
+
+int convrot_linear_multi(const uint16_t* x, int64_t M, int64_t K, int group, int wbits,
+                         const convrot_linear_out* outs, int n_outs, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
+  if (int rc = check_k(K, group, wbits == 4)) return rc;
+  if (M < 0 || M > kMaxRows) return CONVROT_ERR_SHAPE;
+  if (int rc = check_outs(M, outs, n_outs, true)) return rc;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !workspace) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(workspace, 16)) return CONVROT_ERR_ALIGN;
+  if (workspace_bytes < convrot_workspace_size(M, K)) return CONVROT_ERR_WORKSPACE;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* xs = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(size_t(M) * size_t(K), kAlign));
+  hipError_t e = convrot::launch_rotate_quant(x, CONVROT_W_BF16, M, K, log2_group(group), xq, xs, stream);
+  if (e != hipSuccess) return CONVROT_ERR_DEVICE;
+  return device_status(launch_outs(xq, xs, wbits, M, K, outs, n_outs, stream));
 }
 
 }  // extern "C"

@@ -42,6 +42,21 @@ hipError_t launch_rmsnorm_rotate_quant_g256(const uint16_t* x, const float* norm
 hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,
                                      uint8_t* wq4, float* scale, int32_t* clip_index, hipStream_t stream);
 
+// One weight matrix of a GEMM launch and its outputs (row stride ldy
+// elements); acc and y may each be null, the same way for every output.
+struct GemmOutDesc {
+  const void* wq;
+  const float* w_scale;
+  int N, ldy;
+  int32_t* acc;
+  uint16_t* y;
+};
+
+// acc_o = xq . wq_o^T (int32), optional bf16 epilogue, for 1..8 weight
+// matrices sharing the quantized input, in one launch.  wbits 8 or 4.
+hipError_t launch_gemm_multi(const int8_t* xq, const float* x_scale, int wbits, int64_t M, int64_t K,
+                             const GemmOutDesc* outs, int n_outs, hipStream_t stream);
+
 // acc = xq . wq^T (int32), optional bf16 epilogue.  wbits 8 or 4.
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits,
                        const float* w_scale, int64_t M, int64_t N, int64_t K, int32_t* acc_out,

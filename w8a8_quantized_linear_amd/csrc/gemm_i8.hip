@@ -51,6 +51,7 @@
 // and token rows in its L2.
 #include "convrot_internal.h"
 
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
@@ -120,6 +121,26 @@ __device__ __forceinline__ void interleave_phase() {
 //            just freed.
 __device__ __forceinline__ int swz128(int r) { return (r >> 1) & 7; }
 
+// The weight matrices of one launch.  They share the token operand (one
+// quantized activation feeding several linears); their column tiles are
+// concatenated, output o owning column tiles [tn0[o], tn0[o + 1]).  With a
+// single output (MULTI = false) only entry 0 is read, at fixed offsets that
+// the kernel fetches with its other arguments; the multi-output kernels
+// search tn0 and fetch the tile's entry.
+constexpr int kMaxOuts = 8;
+struct GemmOut {
+  const uint8_t* W;  // [N, K] int8 or [N, K/2] packed int4
+  const float* sw;   // [N]
+  int32_t* acc;      // [M, ldy] or null (null for every output, or for none)
+  uint16_t* y;       // [M, ldy] or null (likewise)
+  int N, ldy;
+};
+struct GemmOuts {
+  GemmOut o[kMaxOuts];
+  int tn0[kMaxOuts];  // first column tile of each output (unused entries: INT_MAX)
+  int n;
+};
+
 template <int BM, int BN, bool W4>
 struct CfgK {
   static constexpr int WM = BM / 2, WN = BN / 2;
@@ -145,11 +166,9 @@ struct CfgK {
   static constexpr bool PERSIST = !(BM == 256 && BN == 256);
 };
 
-template <int BM, int BN, bool W4, bool EVEN>
-__device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx,
-                                               const uint8_t* __restrict__ W, const float* __restrict__ sw, int M,
-                                               int N, int K, int tiles_m, int tiles_n, int ldy,
-                                               int32_t* __restrict__ acc_out, uint16_t* __restrict__ y) {
+template <int BM, int BN, bool W4, bool EVEN, bool MULTI>
+__device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx, int M,
+                                               int K, int tiles_m, int tiles_n, const GemmOuts& outs) {
   using C = CfgK<BM, BN, W4>;
   constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS, P2 = C::P2;
   const int Kb = W4 ? K / 2 : K;  // bytes per weight row
@@ -175,14 +194,33 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   const int G = gridDim.x;
   auto tile_of = [&](int v) { return (T & 7) == 0 ? (v & 7) * (T >> 3) + (v >> 3) : v; };
 
-  int m0 = 0, n0 = 0, rows_x = 0, rows_w = 0;
+  // Output of column tile tn (uniform): the number of later outputs whose
+  // first tile it has reached.
+  auto out_of = [&](int tn) {
+    int o = 0;
+    if constexpr (MULTI) {
+#pragma unroll
+      for (int i = 1; i < kMaxOuts; ++i) o += tn >= outs.tn0[i] ? 1 : 0;
+    }
+    return o;
+  };
+  const bool has_acc = outs.o[0].acc != nullptr, has_y = outs.o[0].y != nullptr;
+
+  int m0 = 0, n0 = 0, rows_x = 0, rows_w = 0, cur = 0;
+  const uint8_t* W = outs.o[0].W;
+  const float* sw = outs.o[0].sw;
   __amdgpu_buffer_rsrc_t rsx, rsw;
   auto set_tile = [&](int v) {
     const int t = tile_of(v);
+    const int tn = t / tiles_m;
+    const int o = out_of(tn);
+    cur = o;
+    W = outs.o[o].W;
+    sw = outs.o[o].sw;
     m0 = (t % tiles_m) * BM;
-    n0 = (t / tiles_m) * BN;
+    n0 = (tn - (MULTI ? outs.tn0[o] : 0)) * BN;
     rows_x = min(BM, M - m0);
-    rows_w = min(BN, N - n0);
+    rows_w = min(BN, outs.o[o].N - n0);
     rsx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + int64_t(m0) * K), short(0), rows_x * K,
                                             kBufFlags);
     rsw = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(W + int64_t(n0) * Kb), short(0), rows_w * Kb,
@@ -343,7 +381,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // The tile's weight-row and token scales go to LDS with one 1 KB load each
   // (waves 0 and 1); they are first read in the epilogue.
   auto load_scales = [&]() {
-    if (y && wave < 2) {
+    if (has_y && wave < 2) {
       const float* src = wave == 0 ? sw + n0 : sx + m0;
       const int nrec = 4 * (wave == 0 ? rows_w : rows_x);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
@@ -400,7 +438,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     sync_stage();  // every wave is done with both stage buffers
 
     // Start the next tile's loads so that they land during this epilogue.
-    const int em0 = m0, en0 = n0;
+    const int em0 = m0, en0 = n0, eo = cur;
     const int vn = v + G;
     const bool more = C::PERSIST && vn < T;
     if (more) {
@@ -421,8 +459,12 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     // this block's LDS round trip and stores.
     {
       const int m0 = em0, n0 = en0;
-    if (acc_out) {
-      const bool vec_ok = (N & 3) == 0;
+      // This tile's output (set_tile above has moved on to the next tile).
+      const int N = outs.o[eo].N, ldy = outs.o[eo].ldy;
+      int32_t* const acc_out = outs.o[eo].acc;
+      uint16_t* const y = outs.o[eo].y;
+    if (has_acc) {
+      const bool vec_ok = ((N | ldy) & 3) == 0;
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int m = m0 + wm * WM + j * 32 + row;
@@ -445,14 +487,14 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
           }
       }
     }
-      if (y) {
+      if (has_y) {
         auto chunk_of = [&](int r, int q) {
           if constexpr (NQ == 16) return q ^ (r & 15);
           else if constexpr (NQ == 8) return q ^ ((r >> 1) & 7);
           else return q;
         };
         // Interior tiles (and N a multiple of 8) store without per-element checks.
-        const bool interior = m0 + BM <= M && n0 + BN <= N && (N & 7) == 0;
+        const bool interior = m0 + BM <= M && n0 + BN <= N && ((N | ldy) & 7) == 0;
         // All scales this lane needs, read once: the staging writes below go
         // through a per-wave pointer the compiler cannot separate from the
         // scale arrays, so reads inside the block loop would be repeated.
@@ -499,7 +541,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
             const int n = n0 + wn * WN + 8 * q;
             const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
             if (m < M) {
-              if ((N & 7) == 0 && n + 7 < N) {
+              if (((N | ldy) & 7) == 0 && n + 7 < N) {
                 *reinterpret_cast<uint4*>(y + int64_t(m) * ldy + n) = v;
               } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -533,27 +575,19 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
 }
 
 // K a multiple of 256 (every group-256 linear): unchecked scalar-offset loads.
-template <int BM, int BN, bool W4>
+template <int BM, int BN, bool W4, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_kernel(const int8_t* __restrict__ X,
-                                                                   const float* __restrict__ sx,
-                                                                   const uint8_t* __restrict__ W,
-                                                                   const float* __restrict__ sw, int M, int N, int K,
-                                                                   int tiles_m, int tiles_n, int ldy,
-                                                                   int32_t* __restrict__ acc_out,
-                                                                   uint16_t* __restrict__ y) {
-  gemm_k128_body<BM, BN, W4, true>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, ldy, acc_out, y);
+                                                                   const float* __restrict__ sx, int M, int K,
+                                                                   int tiles_m, int tiles_n, GemmOuts outs) {
+  gemm_k128_body<BM, BN, W4, true, MULTI>(X, sx, M, K, tiles_m, tiles_n, outs);
 }
 
 // Any K (a multiple of 16, of 32 for int4 weights): every chunk range-checked.
-template <int BM, int BN, bool W4>
+template <int BM, int BN, bool W4, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const int8_t* __restrict__ X,
-                                                                        const float* __restrict__ sx,
-                                                                        const uint8_t* __restrict__ W,
-                                                                        const float* __restrict__ sw, int M, int N,
-                                                                        int K, int tiles_m, int tiles_n, int ldy,
-                                                                        int32_t* __restrict__ acc_out,
-                                                                        uint16_t* __restrict__ y) {
-  gemm_k128_body<BM, BN, W4, false>(X, sx, W, sw, M, N, K, tiles_m, tiles_n, ldy, acc_out, y);
+                                                                        const float* __restrict__ sx, int M, int K,
+                                                                        int tiles_m, int tiles_n, GemmOuts outs) {
+  gemm_k128_body<BM, BN, W4, false, MULTI>(X, sx, M, K, tiles_m, tiles_n, outs);
 }
 
 // Workgroups of `kernel` the current device runs at once: compute units x
@@ -585,16 +619,26 @@ int resident_slots(const void* kernel) {
   return slots;
 }
 
-// One band of output columns: y and acc_out have row stride ldy; wq,
-// w_scale, acc_out and y already point at the band's first column.
+// One launch over the outputs in `d` (each a weight matrix with its
+// outputs; all share xq).  Column tiles of the outputs are concatenated.
 template <int BM, int BN, bool W4>
-hipError_t launch_k128(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M, int N,
-                       int K, int ldy, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d, int n,
+                       hipStream_t stream) {
+  GemmOuts outs{};
+  outs.n = n;
+  int tiles_n = 0;
+  for (int o = 0; o < kMaxOuts; ++o) {
+    outs.tn0[o] = o < n ? tiles_n : INT_MAX;
+    if (o < n) {
+      outs.o[o] = {static_cast<const uint8_t*>(d[o].wq), d[o].w_scale, d[o].acc, d[o].y, d[o].N, d[o].ldy};
+      tiles_n += (d[o].N + BN - 1) / BN;
+    }
+  }
   const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  void (*kernel)(const int8_t*, const float*, const uint8_t*, const float*, int, int, int, int, int, int, int32_t*,
-                 uint16_t*) = gemm_i8_k128_tail_kernel<BM, BN, W4>;
-  if (K % 256 == 0) kernel = gemm_i8_k128_kernel<BM, BN, W4>;
+  using Kernel = void (*)(const int8_t*, const float*, int, int, int, int, GemmOuts);
+  const bool even = K % 256 == 0;
+  Kernel kernel = n > 1 ? (even ? gemm_i8_k128_kernel<BM, BN, W4, true> : gemm_i8_k128_tail_kernel<BM, BN, W4, true>)
+                        : (even ? gemm_i8_k128_kernel<BM, BN, W4, false> : gemm_i8_k128_tail_kernel<BM, BN, W4, false>);
   // Persistent configurations: as many workgroups as the device holds at
   // once (never more than there are tiles), each walking its tiles in turn;
   // otherwise one workgroup per tile.
@@ -605,8 +649,7 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, const uint8_t* wq
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
   }
   const dim3 grid(unsigned(tiles < slots ? tiles : slots));
-  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, xq, x_scale, wq, w_scale, M, N, K, tiles_m, tiles_n,
-                     ldy, acc_out, y);
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, xq, x_scale, M, K, tiles_m, tiles_n, outs);
   return hipGetLastError();
 }
 
@@ -639,24 +682,33 @@ struct Plan {
   Band b[2];
 };
 
-// Tile plan for int8 weights, from measurements on MI355X under sustained
-// load.  The chip runs this GEMM below its top clock, and the clock rises
-// when less data moves per MFMA, so the largest tile (256x256: fewest
-// L2->LDS bytes per operation) wins once it fills several whole rounds of
-// the 256 CUs; otherwise 256x192 when it fills at least three quarters of a
-// round, and 128x128 for small problems (more CUs busy).  Splitting N into
-// bands of different tiles to even out a partial round measured no faster
-// than a single 256x192 launch (the second launch waits for the first).
-Plan choose_plan(int64_t M, int64_t N) {
+// Tile plan, from measurements on MI355X under sustained load.  The chip
+// runs this GEMM below its top clock, and the clock rises when less data
+// moves per MFMA, so the largest tile (256x256: fewest L2->LDS bytes per
+// operation) wins once it fills several whole rounds of the 256 CUs;
+// otherwise 256x192 when it fills at least three quarters of a round, and
+// 128x128 for small problems (more CUs busy).  Splitting N into bands of
+// different tiles to even out a partial round measured no faster than a
+// single 256x192 launch (the second launch waits for the first).  With
+// several outputs the tiles of all of them count, and 256x256 needs every
+// output's N to be a multiple of 256.
+TileChoice choose_tile(int64_t M, const GemmOutDesc* d, int n) {
   const int cus = 256;
-  auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (N % 256 == 0 && tiles(256, 256) >= 3 * cus) return {1, {{0, {256, 256}}, {0, {0, 0}}}};
-  if (4 * tiles(256, 192) >= 3 * cus) return {1, {{0, {256, 192}}, {0, {0, 0}}}};
-  return {1, {{0, {128, 128}}, {0, {0, 0}}}};
+  auto tiles = [&](int bm, int bn) {
+    int64_t t = 0;
+    for (int o = 0; o < n; ++o) t += (d[o].N + bn - 1) / bn;
+    return ((M + bm - 1) / bm) * t;
+  };
+  bool n256 = true;
+  for (int o = 0; o < n; ++o) n256 = n256 && d[o].N % 256 == 0;
+  if (n256 && tiles(256, 256) >= 3 * cus) return {256, 256};
+  if (4 * tiles(256, 192) >= 3 * cus) return {256, 192};
+  return {128, 128};
 }
 
-// CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan (a tuning
-// override for sweeps; every plan gives bit-identical results).
+// CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan for a
+// single output (a tuning override for sweeps; every plan gives
+// bit-identical results).
 bool plan_override(Plan& out) {
   static const Plan forced = [] {
     Plan p{0, {{0, {0, 0}}, {0, {0, 0}}}};
@@ -673,46 +725,52 @@ bool plan_override(Plan& out) {
 }
 
 template <bool W4>
-hipError_t launch_band(TileChoice tc, const int8_t* xq, const float* x_scale, const uint8_t* wq,
-                       const float* w_scale, int M, int N, int K, int ldy, int32_t* acc_out, uint16_t* y,
-                       hipStream_t stream) {
-  if (tc.bm == 256 && tc.bn == 256)
-    return launch_k128<256, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
-  if (tc.bm == 256 && tc.bn == 192)
-    return launch_k128<256, 192, W4>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
-  if (tc.bm == 256 && tc.bn == 128)
-    return launch_k128<256, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
-  if (tc.bm == 128 && tc.bn == 256)
-    return launch_k128<128, 256, W4>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
-  return launch_k128<128, 128, W4>(xq, x_scale, wq, w_scale, M, N, K, ldy, acc_out, y, stream);
+hipError_t launch_tile(TileChoice tc, const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d,
+                       int n, hipStream_t stream) {
+  if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256, W4>(xq, x_scale, M, K, d, n, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192, W4>(xq, x_scale, M, K, d, n, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128, W4>(xq, x_scale, M, K, d, n, stream);
+  if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, W4>(xq, x_scale, M, K, d, n, stream);
+  return launch_k128<128, 128, W4>(xq, x_scale, M, K, d, n, stream);
 }
 
 template <bool W4>
-hipError_t launch_plan(const int8_t* xq, const float* x_scale, const uint8_t* wq, const float* w_scale, int M,
-                       int N, int K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
+hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d, int n,
+                       hipStream_t stream) {
   Plan plan;
-  const TileChoice forced = tile_override();
-  if (!plan_override(plan)) plan = forced.bm ? Plan{1, {{0, forced}, {0, {0, 0}}}} : choose_plan(M, N);
-  const int64_t row_bytes = W4 ? K / 2 : K;
-  int n_begin = 0;
-  for (int i = 0; i < plan.nb && n_begin < N; ++i) {
-    const int cols = (plan.b[i].n_cols > 0 && n_begin + plan.b[i].n_cols < N) ? plan.b[i].n_cols : N - n_begin;
-    const hipError_t e = launch_band<W4>(plan.b[i].tc, xq, x_scale, wq + n_begin * row_bytes,
-                                         w_scale ? w_scale + n_begin : nullptr, M, cols, K, N,
-                                         acc_out ? acc_out + n_begin : nullptr, y ? y + n_begin : nullptr, stream);
-    if (e != hipSuccess) return e;
-    n_begin += cols;
+  if (n == 1 && plan_override(plan)) {
+    // Bands of one output's columns, each its own launch (row stride N).
+    const GemmOutDesc& o = d[0];
+    const int64_t row_bytes = W4 ? K / 2 : K;
+    int n_begin = 0;
+    for (int i = 0; i < plan.nb && n_begin < o.N; ++i) {
+      const int cols = (plan.b[i].n_cols > 0 && n_begin + plan.b[i].n_cols < o.N) ? plan.b[i].n_cols : o.N - n_begin;
+      const GemmOutDesc band{static_cast<const uint8_t*>(o.wq) + n_begin * row_bytes,
+                             o.w_scale ? o.w_scale + n_begin : nullptr, cols, o.ldy,
+                             o.acc ? o.acc + n_begin : nullptr, o.y ? o.y + n_begin : nullptr};
+      const hipError_t e = launch_tile<W4>(plan.b[i].tc, xq, x_scale, M, K, &band, 1, stream);
+      if (e != hipSuccess) return e;
+      n_begin += cols;
+    }
+    return hipSuccess;
   }
-  return hipSuccess;
+  const TileChoice forced = tile_override();
+  return launch_tile<W4>(forced.bm ? forced : choose_tile(M, d, n), xq, x_scale, M, K, d, n, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {
-  const uint8_t* w = static_cast<const uint8_t*>(wq);
-  if (wbits == 4) return launch_plan<true>(xq, x_scale, w, w_scale, int(M), int(N), int(K), acc_out, y, stream);
-  return launch_plan<false>(xq, x_scale, w, w_scale, int(M), int(N), int(K), acc_out, y, stream);
+  const GemmOutDesc d{wq, w_scale, int(N), int(N), acc_out, y};
+  return launch_gemm_multi(xq, x_scale, wbits, M, K, &d, 1, stream);
+}
+
+hipError_t launch_gemm_multi(const int8_t* xq, const float* x_scale, int wbits, int64_t M, int64_t K,
+                             const GemmOutDesc* outs, int n_outs, hipStream_t stream) {
+  if (n_outs < 1 || n_outs > kMaxOuts) return hipErrorInvalidValue;
+  if (wbits == 4) return launch_plan<true>(xq, x_scale, int(M), int(K), outs, n_outs, stream);
+  return launch_plan<false>(xq, x_scale, int(M), int(K), outs, n_outs, stream);
 }
 
 }  // namespace convrot
