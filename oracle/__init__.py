@@ -70,6 +70,8 @@ def _load():
         "oracle_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P]),
         "oracle_rmsnorm_bf16": (I, [P, P, ctypes.c_float, I64, I64, P]),
         "oracle_rmsnorm_rotate_quant": (I, [P, P, ctypes.c_float, I64, I64, I, P, P, P]),
+        "oracle_dequantize_weight": (I, [P, P, I64, I64, I, P]),
+        "oracle_gemm_bf16": (I, [P, P, I64, I64, I64, P]),
         "oracle_num_threads": (I, []),
     }
     for name, (res, args) in sigs.items():
@@ -230,3 +232,35 @@ def rmsnorm_rotate_quant(x_bf16: np.ndarray, w: np.ndarray, eps: float = 1e-6, g
     _check(_load().oracle_rmsnorm_rotate_quant(_ptr(x), _ptr(w), float(eps), M, K, int(group), _ptr(xq), _ptr(s),
                                                _ptr(y)), "rmsnorm_rotate_quant")
     return xq, s, y
+
+
+def dequantize_weight(wq: np.ndarray, w_scale: np.ndarray, group: int = 256) -> np.ndarray:
+    """Weight-only path: int8 codes [N, K] (or packed int4 uint8 [N, K/2]) and
+    fp32 row scales -> the dequantized, un-rotated weight as bf16 bits [N, K]."""
+    wq = np.ascontiguousarray(wq)
+    if wq.dtype == np.uint8:
+        wq = unpack_i4(wq)
+    wq = np.ascontiguousarray(wq, dtype=np.int8)
+    s = np.ascontiguousarray(w_scale, dtype=np.float32)
+    N, K = wq.shape
+    assert s.shape == (N,)
+    out = np.empty((N, K), dtype=np.uint16)
+    _check(_load().oracle_dequantize_weight(_ptr(wq), _ptr(s), N, K, int(group), _ptr(out)), "dequantize_weight")
+    return out
+
+
+def gemm_bf16(x_bf16: np.ndarray, w_bf16: np.ndarray) -> np.ndarray:
+    """bf16 bits [M, K] x bf16 bits [N, K] -> bf16 bits [M, N] (fp64 sum, then fp32, then bf16)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bf16, dtype=np.uint16)
+    M, K = x.shape
+    N = w.shape[0]
+    assert w.shape == (N, K)
+    y = np.empty((M, N), dtype=np.uint16)
+    _check(_load().oracle_gemm_bf16(_ptr(x), _ptr(w), M, N, K, _ptr(y)), "gemm_bf16")
+    return y
+
+
+def dequant_linear(x_bf16: np.ndarray, wq: np.ndarray, w_scale: np.ndarray, group: int = 256) -> np.ndarray:
+    """The weight-only linear: dequantize, then the bf16 matmul with the unrotated input."""
+    return gemm_bf16(x_bf16, dequantize_weight(wq, w_scale, group))

@@ -37,6 +37,9 @@
  *    0.01; scale = c * absmax / 7; the c with the smallest sum of squared
  *    reconstruction error wins (ties to the larger c); byte j of a row holds
  *    column 2j in its low nibble and column 2j+1 in its high nibble.
+ *  - Weight-only (dequant) path ([P1] row "Matmul", [P2]): W^ = (wq * s_w)
+ *    * H in fp64, rounded to fp32 and then to bf16; then a bf16 matmul whose
+ *    sum is taken in fp64 and rounded to fp32 and then to bf16.
  *  - RMSNorm before the linear ([P1] rows "Changed" and "How it was made":
  *    SmoothQuant scales folded into the norm weight as (1 + w) / s - 1): the
  *    norm multiplies by (1 + w); mean square over the whole row, eps inside
@@ -409,6 +412,66 @@ int oracle_rmsnorm_rotate_quant(const uint16_t *x, const float *w, float eps, in
     int rc = oracle_rmsnorm_bf16(x, w, eps, M, K, y);
     if (rc == ORACLE_OK) rc = oracle_rotate_quant(y, M, K, g, xq, x_scale);
     return rc;
+}
+
+/* ------------------------------------------------ weight-only dequant path */
+
+/* The weight-only runtime mode ([P1] file table, row "Matmul": the weight can
+ * instead be dequantized for a bf16 matmul; [P2] loads the checkpoints
+ * through that dequant path).  A stored row holds the codes of the ROTATED
+ * weight row, so the weight is recovered by undoing the rotation:
+ * W^ = (wq * s_w) * H^-1, and H^-1 = H (the normalised Sylvester matrix is
+ * symmetric and orthogonal).  Per row n and group of g columns:
+ *   v_j      = code_j * s_w[n]                  (fp64; exact)
+ *   u_k      = sum_j v_j * H[j][k]              (fp64 dense product; exact for
+ *                                                even log2(g), where every
+ *                                                entry is +-2^-m)
+ *   W^[n][k] = bf16_rne((float)u_k)             (rounded to fp32, the scale's
+ *                                                precision, then to bf16)
+ * int4 rows are unpacked to their codes first (oracle_unpack_i4). */
+int oracle_dequantize_weight(const int8_t *wq, const float *w_scale, int64_t N, int64_t K, int g, uint16_t *w_out) {
+    if (!wq || !w_scale || !w_out || N < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
+    if (!H) return ORACLE_ERR_ARG;
+    oracle_hadamard(g, H);
+    int rc = ORACLE_OK;
+#pragma omp parallel
+    {
+        double *v = (double *)malloc(sizeof(double) * (size_t)K);
+        double *u = (double *)malloc(sizeof(double) * (size_t)K);
+        if (!v || !u) {
+#pragma omp atomic write
+            rc = ORACLE_ERR_ARG;
+        } else {
+#pragma omp for schedule(static)
+            for (int64_t n = 0; n < N; ++n) {
+                for (int64_t k = 0; k < K; ++k) v[k] = (double)wq[n * K + k] * (double)w_scale[n];
+                rotate_row_f64(v, K, g, H, u);
+                for (int64_t k = 0; k < K; ++k) w_out[n * K + k] = float_to_bf16_rne((float)u[k]);
+            }
+        }
+        free(v);
+        free(u);
+    }
+    free(H);
+    return rc;
+}
+
+/* The bf16 matmul of the dequant path: y[m][n] = bf16_rne((float)s) with
+ * s = sum_k x[m][k] * w[n][k] accumulated in fp64 in k order (each product
+ * of two bf16 values is exact in fp64), rounded to fp32 and then to bf16. */
+int oracle_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K, uint16_t *y) {
+    if (!x || !w || !y || M < 0 || N < 0 || K <= 0) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += bf16_bits_to_double(x[m * K + k]) * bf16_bits_to_double(w[n * K + k]);
+            y[m * N + n] = float_to_bf16_rne((float)acc);
+        }
+    }
+    return ORACLE_OK;
 }
 
 /* Number of OpenMP threads a parallel region here would use. */

@@ -549,3 +549,128 @@ def test_rmsnorm_rotate_quant_is_the_composition(oracle_mod):
     assert np.array_equal(y, oracle_mod.rmsnorm(xb, w, 1e-6))
     xq2, s2 = oracle_mod.rotate_quant(y, 256)
     assert np.array_equal(xq, xq2) and np.array_equal(s, s2)
+
+
+# ------------------------------------------------ weight-only dequant path
+
+def _bf16_of_f32(v32):
+    """fp32 values -> bf16 bits via torch's CPU cast (round to nearest even)."""
+    return wl.float_to_bf16_bits(np.asarray(v32, dtype=np.float32))
+
+
+@pytest.mark.parametrize("g", [1, 4, 16, 64, 256])
+def test_dequant_one_hot_closed_form(oracle_mod, g):
+    """A single code c at column j of group b with scale s dequantizes to
+    c*s*H[j][k]/sqrt(g) on that group's columns (Sylvester signs from
+    scipy) and to zero elsewhere."""
+    K = 2 * max(g, 16) if g < 256 else 512
+    K -= K % g
+    for b, j, c, s in [(0, 0, 127, 0.5), (K // g - 1, g - 1, -77, 2.0 ** -10), (K // g // 2, g // 3, 5, 3.0)]:
+        q = np.zeros((1, K), np.int8)
+        q[0, b * g + j] = c
+        got = wl.bf16_bits_to_float(oracle_mod.dequantize_weight(q, np.array([s], np.float32), g))[0]
+        want = np.zeros(K, np.float32)
+        signs = scipy.linalg.hadamard(g)[j] if g > 1 else np.ones(1)
+        want[b * g:(b + 1) * g] = np.float32(c * s / np.sqrt(g)) * signs
+        assert np.array_equal(got, wl.bf16_bits_to_float(_bf16_of_f32(want)))
+
+
+def test_dequant_group_one_is_scale_times_code(oracle_mod):
+    rng = np.random.default_rng(3)
+    q = rng.integers(-127, 128, (5, 64), dtype=np.int8)
+    s = (rng.random(5) * 0.03 + 1e-4).astype(np.float32)
+    got = oracle_mod.dequantize_weight(q, s, 1)
+    want = _bf16_of_f32(q.astype(np.float32) * s[:, None])   # each product is exact in fp32
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("g", [16, 256])
+def test_dequant_inverts_quantize_within_bound(oracle_mod, g):
+    """Orthogonality: the un-rotated reconstruction error of a row equals the
+    rotated one, which is at most sqrt(K) s / 2 for round-to-nearest codes;
+    the bf16 rounding adds at most 2^-9 of the row's norm."""
+    rng = np.random.default_rng(11)
+    N, K = 16, 1024
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    w[:, 7] *= 30.0                                            # an outlier column
+    q, s = oracle_mod.quantize_weight_i8(w, g)
+    back = wl.bf16_bits_to_float(oracle_mod.dequantize_weight(q, s, g)).astype(np.float64)
+    err = np.linalg.norm(back - w, axis=1)
+    bound = np.sqrt(K) * s / 2 + 2.0 ** -9 * np.linalg.norm(back, axis=1) + 1e-6 * np.linalg.norm(w, axis=1)
+    assert np.all(err <= bound)
+    assert np.all(err >= 0.05 * np.sqrt(K) * s / 2)             # the codes' rounding is really there
+
+
+def test_dequant_int4_error_is_the_clip_search_error(oracle_mod):
+    """Parseval: for packed int4 rows the un-rotated reconstruction error
+    equals the rotated-domain error of the chosen codes, up to bf16 rounding."""
+    rng = np.random.default_rng(12)
+    N, K = 8, 512
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    packed, s, _ = oracle_mod.quantize_weight_i4(w, 256)
+    back = wl.bf16_bits_to_float(oracle_mod.dequantize_weight(packed, s, 256)).astype(np.float64)
+    lo, hi = ref_unpack(packed)
+    codes = np.stack([lo, hi], axis=-1).reshape(N, K).astype(np.float64)   # low nibble = even column
+    rot = ref_rotate(w.astype(np.float64), 256)
+    e_rot = np.linalg.norm(codes * s[:, None].astype(np.float64) - rot, axis=1)
+    e_back = np.linalg.norm(back - w, axis=1)
+    slack = 2.0 ** -9 * np.linalg.norm(back, axis=1) + 1e-6
+    assert np.all(np.abs(e_back - e_rot) <= slack)
+
+
+def _exact_bf16_products(rng, shape, exp_lo=-3, exp_hi=3):
+    """bf16 values whose products and sums are exact in fp64 (7-bit mantissas,
+    exponents in a narrow band)."""
+    mant = rng.integers(128, 256, shape) * rng.choice([-1, 1], shape)
+    e = rng.integers(exp_lo, exp_hi + 1, shape)
+    v = (mant * np.exp2(e - 7)).astype(np.float32)
+    v[rng.random(shape) < 0.1] = 0.0
+    return _bf16_of_f32(v)
+
+
+@pytest.mark.parametrize("M,N,K,seed", [(1, 1, 1, 0), (3, 4, 17, 1), (5, 7, 64, 2), (2, 9, 300, 3)])
+def test_gemm_bf16_brute_force_tiny(oracle_mod, M, N, K, seed):
+    """Exact rational sums, rounded to fp32 and then to bf16."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    x = _exact_bf16_products(rng, (M, K))
+    w = _exact_bf16_products(rng, (N, K))
+    xf = wl.bf16_bits_to_float(x)
+    wf = wl.bf16_bits_to_float(w)
+    want = np.empty((M, N), np.float32)
+    for m in range(M):
+        for n in range(N):
+            exact = sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xf[m], wf[n])), Fraction(0))
+            want[m, n] = np.float32(float(exact))                 # exact in fp64 here, then one fp32 rounding
+    assert np.array_equal(oracle_mod.gemm_bf16(x, w), _bf16_of_f32(want))
+
+
+def test_gemm_bf16_identity_and_rounding_order(oracle_mod):
+    """x = I returns W exactly; and a sum just above a bf16 tie, whose fp32
+    rounding lands on the tie, rounds to even (fp32 first, then bf16)."""
+    rng = np.random.default_rng(4)
+    K = 32
+    w = _bf16_of_f32(rng.standard_normal((6, K)).astype(np.float32))
+    eye = _bf16_of_f32(np.eye(K, dtype=np.float32))
+    assert np.array_equal(oracle_mod.gemm_bf16(eye, w), w.T.copy())
+    x = _bf16_of_f32(np.array([[1.0, 2.0 ** -8, 2.0 ** -30]], np.float32))
+    ones = _bf16_of_f32(np.ones((1, 3), np.float32))
+    assert wl.bf16_bits_to_float(oracle_mod.gemm_bf16(x, ones))[0, 0] == 1.0
+
+
+def test_dequant_linear_is_the_composition(oracle_mod):
+    rng = np.random.default_rng(5)
+    x = bf16(rng.standard_normal((4, 512)))
+    q = rng.integers(-127, 128, (6, 512), dtype=np.int8)
+    s = (rng.random(6) * 0.01).astype(np.float32)
+    assert np.array_equal(oracle_mod.dequant_linear(x, q, s, 256),
+                          oracle_mod.gemm_bf16(x, oracle_mod.dequantize_weight(q, s, 256)))
+
+
+def test_gemm_bf16_sum_carries_fp64(oracle_mod):
+    """2^25 + 200 ones - 2^25: the exact sum 200 survives an fp64 sum (an fp32
+    one would lose every 1 next to 2^25)."""
+    vals = np.array([2.0 ** 25] + [1.0] * 200 + [-(2.0 ** 25)], np.float32)
+    x = _bf16_of_f32(vals[None, :])
+    ones = _bf16_of_f32(np.ones((1, vals.size), np.float32))
+    assert wl.bf16_bits_to_float(oracle_mod.gemm_bf16(x, ones))[0, 0] == 200.0

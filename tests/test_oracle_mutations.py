@@ -44,6 +44,14 @@ MUTANTS = [
     ("rmsnorm_eps_outside_root", "const float r = 1.0f / sqrtf(ms + eps);",
      "const float r = 1.0f / (sqrtf(ms) + eps);"),
     ("rmsnorm_mean_abs", "ss += v * v;", "ss += fabs(v) * fabs(v) * (v < 0 ? 0.5 : 1.0);"),
+    ("dequant_no_scale", "v[k] = (double)wq[n * K + k] * (double)w_scale[n];", "v[k] = (double)wq[n * K + k];"),
+    ("dequant_skips_rotation", "rotate_row_f64(v, K, g, H, u);", "memcpy(u, v, sizeof(double) * (size_t)K);"),
+    ("dequant_rows_swapped", "v[k] = (double)wq[n * K + k] * (double)w_scale[n];",
+     "v[k] = (double)wq[n * K + k] * (double)w_scale[N - 1 - n];"),
+    ("gemm_bf16_drops_last_k", "for (int64_t k = 0; k < K; ++k)\n                acc += bf16_bits_to_double",
+     "for (int64_t k = 0; k + 1 < K; ++k)\n                acc += bf16_bits_to_double"),
+    ("gemm_bf16_fp32_accumulation", "double acc = 0.0;\n            for (int64_t k = 0; k < K; ++k)\n                acc += bf16",
+     "float acc = 0.0f;\n            for (int64_t k = 0; k < K; ++k)\n                acc += bf16"),
 ]
 
 PIN_TESTS = [
@@ -61,19 +69,29 @@ PIN_TESTS = [
     "test_rmsnorm_constant_power_of_two_rows", "test_rmsnorm_one_hot_gives_sqrt_k",
     "test_rmsnorm_weight_enters_as_one_plus_w", "test_rmsnorm_eps_inside_the_root",
     "test_rmsnorm_zero_row_and_unit_rms",
+    "test_dequant_one_hot_closed_form", "test_dequant_group_one_is_scale_times_code",
+    "test_dequant_inverts_quantize_within_bound", "test_dequant_int4_error_is_the_clip_search_error",
+    "test_gemm_bf16_brute_force_tiny", "test_gemm_bf16_identity_and_rounding_order",
+    "test_gemm_bf16_sum_carries_fp64",
 ]
 
 
 def _run_pin(name):
+    """Run one pin as pytest would: every parameter set of its parametrize
+    mark (tests drawn by hypothesis generate their own arguments)."""
     fn = getattr(pins, name)
     import inspect
     params = inspect.signature(fn).parameters
-    if "g" in params:  # parametrised over group sizes
-        for g in (2, 16, 256):
-            fn(oracle, g)
-    elif "K" in params:  # parametrised over row lengths
-        for K in (256, 1024):
-            fn(oracle, K)
+    marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+    if marks:
+        argnames, argvalues = marks[0].args[0], marks[0].args[1]
+        names = [a.strip() for a in argnames.split(",")] if isinstance(argnames, str) else list(argnames)
+        for vals in argvalues:
+            vals = vals if len(names) > 1 else (vals,)
+            kwargs = dict(zip(names, vals))
+            if "oracle_mod" in params:
+                kwargs["oracle_mod"] = oracle
+            fn(**kwargs)
     elif "oracle_mod" in params:
         fn(oracle)
     else:
