@@ -38,8 +38,9 @@
  *    reconstruction error wins (ties to the larger c); byte j of a row holds
  *    column 2j in its low nibble and column 2j+1 in its high nibble.
  *  - Weight-only (dequant) path ([P1] row "Matmul", [P2]): W^ = (wq * s_w)
- *    * H in fp64, rounded to fp32 and then to bf16; then a bf16 matmul whose
- *    sum is taken in fp64 and rounded to fp32 and then to bf16.
+ *    * H, computed as the exact +-1 transform of the codes times s_w times
+ *    1/sqrt(g) in fp64, rounded to fp32 and then to bf16; then a bf16 matmul
+ *    whose sum is taken in fp64 and rounded to fp32 and then to bf16.
  *  - RMSNorm before the linear ([P1] rows "Changed" and "How it was made":
  *    SmoothQuant scales folded into the norm weight as (1 + w) / s - 1): the
  *    norm multiplies by (1 + w); mean square over the whole row, eps inside
@@ -421,40 +422,38 @@ int oracle_rmsnorm_rotate_quant(const uint16_t *x, const float *w, float eps, in
  * through that dequant path).  A stored row holds the codes of the ROTATED
  * weight row, so the weight is recovered by undoing the rotation:
  * W^ = (wq * s_w) * H^-1, and H^-1 = H (the normalised Sylvester matrix is
- * symmetric and orthogonal).  Per row n and group of g columns:
- *   v_j      = code_j * s_w[n]                  (fp64; exact)
- *   u_k      = sum_j v_j * H[j][k]              (fp64 dense product; exact for
- *                                                even log2(g), where every
- *                                                entry is +-2^-m)
+ * symmetric and orthogonal).  Written with the scalar factors of that
+ * product taken out, so that it is exact wherever it can be:
+ *   t_k      = sum_j code_j * sign(H[j][k])     (the +-1 pattern; an exact
+ *                                                integer, |t| <= 256 * 128)
+ *   u_k      = (t_k * s_w[n]) * H[0][0]         (fp64; H[0][0] = 1/sqrt(g),
+ *                                                a power of two, so exact,
+ *                                                for even log2(g))
  *   W^[n][k] = bf16_rne((float)u_k)             (rounded to fp32, the scale's
  *                                                precision, then to bf16)
- * int4 rows are unpacked to their codes first (oracle_unpack_i4). */
+ * per group of g columns.  int4 rows are unpacked to their codes first
+ * (oracle_unpack_i4). */
 int oracle_dequantize_weight(const int8_t *wq, const float *w_scale, int64_t N, int64_t K, int g, uint16_t *w_out) {
     if (!wq || !w_scale || !w_out || N < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
     double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
     if (!H) return ORACLE_ERR_ARG;
     oracle_hadamard(g, H);
-    int rc = ORACLE_OK;
-#pragma omp parallel
-    {
-        double *v = (double *)malloc(sizeof(double) * (size_t)K);
-        double *u = (double *)malloc(sizeof(double) * (size_t)K);
-        if (!v || !u) {
-#pragma omp atomic write
-            rc = ORACLE_ERR_ARG;
-        } else {
-#pragma omp for schedule(static)
-            for (int64_t n = 0; n < N; ++n) {
-                for (int64_t k = 0; k < K; ++k) v[k] = (double)wq[n * K + k] * (double)w_scale[n];
-                rotate_row_f64(v, K, g, H, u);
-                for (int64_t k = 0; k < K; ++k) w_out[n * K + k] = float_to_bf16_rne((float)u[k]);
+    const double norm = H[0];
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t *q = wq + n * K;
+        for (int64_t base = 0; base < K; base += g) {
+            for (int k = 0; k < g; ++k) {
+                double t = 0.0;
+                for (int j = 0; j < g; ++j)
+                    t += (H[(int64_t)j * g + k] > 0.0 ? 1.0 : -1.0) * (double)q[base + j];
+                const double u = (t * (double)w_scale[n]) * norm;
+                w_out[n * K + base + k] = float_to_bf16_rne((float)u);
             }
         }
-        free(v);
-        free(u);
     }
     free(H);
-    return rc;
+    return ORACLE_OK;
 }
 
 /* The bf16 matmul of the dequant path: y[m][n] = bf16_rne((float)s) with

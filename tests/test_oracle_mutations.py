@@ -44,10 +44,13 @@ MUTANTS = [
     ("rmsnorm_eps_outside_root", "const float r = 1.0f / sqrtf(ms + eps);",
      "const float r = 1.0f / (sqrtf(ms) + eps);"),
     ("rmsnorm_mean_abs", "ss += v * v;", "ss += fabs(v) * fabs(v) * (v < 0 ? 0.5 : 1.0);"),
-    ("dequant_no_scale", "v[k] = (double)wq[n * K + k] * (double)w_scale[n];", "v[k] = (double)wq[n * K + k];"),
-    ("dequant_skips_rotation", "rotate_row_f64(v, K, g, H, u);", "memcpy(u, v, sizeof(double) * (size_t)K);"),
-    ("dequant_rows_swapped", "v[k] = (double)wq[n * K + k] * (double)w_scale[n];",
-     "v[k] = (double)wq[n * K + k] * (double)w_scale[N - 1 - n];"),
+    ("dequant_no_scale", "const double u = (t * (double)w_scale[n]) * norm;", "const double u = t * norm;"),
+    ("dequant_skips_rotation", "t += (H[(int64_t)j * g + k] > 0.0 ? 1.0 : -1.0) * (double)q[base + j];",
+     "t += (j == k ? 1.0 : 0.0) * (double)q[base + j];"),
+    ("dequant_rows_swapped", "const double u = (t * (double)w_scale[n]) * norm;",
+     "const double u = (t * (double)w_scale[N - 1 - n]) * norm;"),
+    ("dequant_sign_transposed_block", "t += (H[(int64_t)j * g + k] > 0.0 ? 1.0 : -1.0) * (double)q[base + j];",
+     "t += (H[(int64_t)j * g + ((k + 1) % g)] > 0.0 ? 1.0 : -1.0) * (double)q[base + j];"),
     ("gemm_bf16_drops_last_k", "for (int64_t k = 0; k < K; ++k)\n                acc += bf16_bits_to_double",
      "for (int64_t k = 0; k + 1 < K; ++k)\n                acc += bf16_bits_to_double"),
     ("gemm_bf16_fp32_accumulation", "double acc = 0.0;\n            for (int64_t k = 0; k < K; ++k)\n                acc += bf16",
