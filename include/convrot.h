@@ -69,7 +69,7 @@ enum convrot_status {
   CONVROT_ERR_SHAPE = 2,     /* M < 0, N <= 0, K <= 0, K % 16, K % group, K % 32 for int4, K or M/N too large */
   CONVROT_ERR_GROUP = 3,     /* group is not a power of two in [1, 256] */
   CONVROT_ERR_ALIGN = 4,     /* a tensor pointer is not 16-byte aligned (scales: 4-byte) */
-  CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than convrot_workspace_size() */
+  CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than the call's workspace-size function gives */
   CONVROT_ERR_DEVICE = 6,    /* the HIP runtime reported an error while enqueueing */
   CONVROT_ERR_DTYPE = 7,     /* unsupported w_dtype or bits value */
   CONVROT_ERR_ARG = 8        /* a scalar argument is out of range (eps negative, NaN or infinite;
@@ -194,6 +194,52 @@ int convrot_gemm_i8(const int8_t *xq, const float *x_scale, const void *wq, int 
  */
 int convrot_quantize_weight_i4_clip(const void *w, int w_dtype, int64_t N, int64_t K, int group, uint8_t *wq4,
                                     float *w_scale, int32_t *clip_index, hipStream_t stream);
+
+/*
+ * Weight-only (dequant) path ("MOSS-Image ... INT8" page, file table row
+ * "Matmul": the weight can instead be dequantized for a bf16 matmul;
+ * "qwen3.5_4b_int8_convrot" loads the checkpoints through that path).  The
+ * activations are not quantized.
+ */
+
+/*
+ * convrot_dequantize_weight -- undo the rotation of stored codes:
+ *   W^[n][k] = bf16(fp32(sum_j code[n][j] * w_scale[n] * H[j][k]))  per group,
+ * the inverse of convrot_quantize_weight up to its rounding (H is its own
+ * inverse).  The codes' transform is exact; for even log2(group) the value
+ * is rounded once to fp32 (then to bf16), for odd log2(group) the 1/sqrt(g)
+ * adds one fp32 rounding.
+ *   wq      : int8 [N, K] (wbits 8) or uint8 [N, K/2] (wbits 4, K % 32 == 0)
+ *   w_scale : fp32 [N]
+ *   w_out   : bf16 bits [N, K]   (written)
+ */
+int convrot_dequantize_weight(const void *wq, int wbits, const float *w_scale, int64_t N, int64_t K, int group,
+                              uint16_t *w_out, hipStream_t stream);
+
+/*
+ * convrot_gemm_bf16 -- y = bf16_rne(x . w^T) with fp32 accumulation on the
+ * matrix cores (v_mfma_f32_32x32x16_bf16); the summation order is the
+ * hardware's, so y differs from the exactly rounded product by the fp32
+ * accumulation error (at most about K * 2^-24 * sum|x*w| per output).
+ *   x : bf16 bits [M, K], w : bf16 bits [N, K], y : bf16 bits [M, N]
+ */
+int convrot_gemm_bf16(const uint16_t *x, const uint16_t *w, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                      hipStream_t stream);
+
+/* Workspace bytes convrot_dequant_linear needs: the bf16 weight, rounded up
+ * to 256 bytes.  0 for N <= 0 or K <= 0. */
+size_t convrot_dequant_workspace_size(int64_t N, int64_t K);
+
+/*
+ * convrot_dequant_linear -- the weight-only linear: dequantize wq into the
+ * workspace (convrot_dequantize_weight), then y = convrot_gemm_bf16(x, W^).
+ * Arguments as convrot_w8a8_linear / convrot_w4a8_linear (wbits 8 or 4);
+ * workspace: at least convrot_dequant_workspace_size(N, K) bytes, 16-byte
+ * aligned.  A caller that keeps W^ resident calls convrot_gemm_bf16 alone.
+ */
+int convrot_dequant_linear(const uint16_t *x, int64_t M, int64_t K, const void *wq, int wbits,
+                           const float *w_scale, int64_t N, int group, uint16_t *y, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Several linears that read the same input: the q, k and v projections of an

@@ -218,3 +218,32 @@ def test_multi_validation(L):
 def test_single_gemm_tile_count_bound(L):
     """M and N each within 2^30 but too many 128 x 128 tiles together."""
     assert gemm(A, B, C, 8, D, 1 << 30, 1 << 20, 64, E, NUL) == ERR["shape"]
+
+
+def test_dequant_path_validation(L):
+    Lb = cr.load()
+    dq = lambda w, wb, s, N, K, g, o: Lb.convrot_dequantize_weight(w, wb, s, N, K, g, o, S0)
+    gb = lambda x, w, M, N, K, y: Lb.convrot_gemm_bf16(x, w, M, N, K, y, S0)
+    dl = lambda x, M, K, w, wb, s, N, g, y, ws, wsb: Lb.convrot_dequant_linear(x, M, K, w, wb, s, N, g, y, ws, wsb, S0)
+    assert dq(A, 3, B, 4, 256, 256, C) == ERR["dtype"]
+    assert dq(A, 8, B, 4, 250, 256, C) == ERR["shape"]
+    assert dq(A, 4, B, 4, 272, 16, C) == ERR["shape"]       # int4 needs K % 32
+    assert dq(A, 8, B, 4, 256, 3, C) == ERR["group"]
+    assert dq(A, 8, B, -1, 256, 256, C) == ERR["shape"]
+    assert dq(NUL, 8, B, 4, 256, 256, C) == ERR["null"]
+    assert dq(A, 8, B, 4, 256, 256, MIS) == ERR["align"]
+    assert dq(NUL, 8, NUL, 0, 256, 256, NUL) == 0
+    assert gb(A, B, 4, 0, 64, C) == ERR["shape"]
+    assert gb(A, B, 4, 4, 40, C) == ERR["shape"]
+    assert gb(A, B, 4, 4, 65536, C) == ERR["shape"]
+    assert gb(A, NUL, 4, 4, 64, C) == ERR["null"]
+    assert gb(A, B, 4, 4, 64, MIS) == ERR["align"]
+    assert gb(NUL, NUL, 0, 4, 64, NUL) == 0
+    assert cr.convrot_dequant_workspace_size(0, 64) == 0
+    assert cr.convrot_dequant_workspace_size(3, 64) == 512
+    need = cr.convrot_dequant_workspace_size(64, 512)
+    assert dl(A, 8, 512, B, 8, C, 64, 256, D, E, need - 1) == ERR["ws"]
+    assert dl(A, 8, 512, B, 5, C, 64, 256, D, E, need) == ERR["dtype"]
+    assert dl(A, 8, 512, B, 8, NUL, 64, 256, D, E, need) == ERR["null"]
+    assert dl(A, 8, 512, B, 8, C, 64, 256, D, MIS, need) == ERR["align"]
+    assert dl(NUL, 0, 512, NUL, 8, NUL, 64, 256, NUL, NUL, 0) == 0

@@ -20,9 +20,11 @@ __all__ = [
     "load", "library_path", "ConvRotError", "LinearOut", "MAX_OUTS",
     "convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
     "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear",
-    "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi", "convrot_status_string", "convrot_version",
+    "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi", "convrot_dequantize_weight",
+    "convrot_gemm_bf16", "convrot_dequant_workspace_size", "convrot_dequant_linear",
+    "convrot_status_string", "convrot_version",
     "quantize_weight", "rotate_quant", "rmsnorm_rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8",
-    "gemm_i8_multi", "linear_multi", "workspace",
+    "gemm_i8_multi", "linear_multi", "dequantize_weight", "gemm_bf16", "dequant_linear", "workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,10 @@ def load():
         "convrot_gemm_i8": (I, [P, P, P, I, P, I64, I64, I64, P, P, P]),
         "convrot_gemm_i8_multi": (I, [P, P, I, I64, I64, P, I, P]),
         "convrot_linear_multi": (I, [P, I64, I64, I, I, P, I, P, SZ, P]),
+        "convrot_dequantize_weight": (I, [P, I, P, I64, I64, I, P, P]),
+        "convrot_gemm_bf16": (I, [P, P, I64, I64, I64, P, P]),
+        "convrot_dequant_workspace_size": (SZ, [I64, I64]),
+        "convrot_dequant_linear": (I, [P, I64, I64, P, I, P, I64, I, P, P, SZ, P]),
         "convrot_status_string": (ctypes.c_char_p, [I]),
         "convrot_version": (I, []),
     }
@@ -89,7 +95,8 @@ def exported_symbols():
     return ["convrot_quantize_weight", "convrot_quantize_weight_i4_clip", "convrot_rotate_quant",
             "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear",
             "convrot_w4a8_linear", "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi",
-            "convrot_status_string", "convrot_version"]
+            "convrot_dequantize_weight", "convrot_gemm_bf16", "convrot_dequant_workspace_size",
+            "convrot_dequant_linear", "convrot_status_string", "convrot_version"]
 
 
 # ------------------------------------------------------------ marshalling
@@ -179,6 +186,25 @@ def convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, workspace, workspace
 def convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc_out, y, stream=None) -> int:
     return load().convrot_gemm_i8(_dptr(xq), _dptr(x_scale), _dptr(wq), int(wbits), _dptr(w_scale), int(M),
                                   int(N), int(K), _dptr(acc_out), _dptr(y), _stream(stream))
+
+
+def convrot_dequantize_weight(wq, wbits, w_scale, N, K, group, w_out, stream=None) -> int:
+    return load().convrot_dequantize_weight(_dptr(wq), int(wbits), _dptr(w_scale), int(N), int(K), int(group),
+                                            _dptr(w_out), _stream(stream))
+
+
+def convrot_gemm_bf16(x, w, M, N, K, y, stream=None) -> int:
+    return load().convrot_gemm_bf16(_dptr(x), _dptr(w), int(M), int(N), int(K), _dptr(y), _stream(stream))
+
+
+def convrot_dequant_workspace_size(N: int, K: int) -> int:
+    return int(load().convrot_dequant_workspace_size(int(N), int(K)))
+
+
+def convrot_dequant_linear(x, M, K, wq, wbits, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    return load().convrot_dequant_linear(_dptr(x), int(M), int(K), _dptr(wq), int(wbits), _dptr(w_scale), int(N),
+                                         int(group), _dptr(y), _dptr(workspace), int(workspace_bytes),
+                                         _stream(stream))
 
 
 def _outs_array(outs):
@@ -287,6 +313,40 @@ def gemm_i8_multi(xq, x_scale, weights, wbits: int = 8, want_acc: bool = True, w
         desc.append((wq, wsc, n, acc, y))
     _check("convrot_gemm_i8_multi", convrot_gemm_i8_multi(xq, x_scale, wbits, M, K, desc))
     return res
+
+
+def dequantize_weight(wq, w_scale, K: int, wbits: int = 8, group: int = 256):
+    """Codes (int8 [N, K] or packed int4 uint8 [N, K/2]) -> bf16 weight [N, K]."""
+    torch = _torch()
+    N = wq.shape[0]
+    out = torch.empty((N, K), dtype=torch.bfloat16, device=wq.device)
+    _check("convrot_dequantize_weight", convrot_dequantize_weight(wq, wbits, w_scale, N, K, group, out))
+    return out
+
+
+def gemm_bf16(x, w, out=None):
+    """bf16 x [M, K] . w [N, K]^T -> bf16 [M, N] (fp32 accumulation)."""
+    torch = _torch()
+    x, w = _bits16(x), _bits16(w)
+    M, K = x.shape
+    N = w.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check("convrot_gemm_bf16", convrot_gemm_bf16(x, w, M, N, K, y))
+    return y
+
+
+def dequant_linear(x, wq, w_scale, wbits: int = 8, group: int = 256, out=None, ws=None):
+    """The weight-only linear: dequantize wq (into a workspace), then the bf16 matmul."""
+    torch = _torch()
+    x = _bits16(x)
+    M, K = x.shape
+    N = wq.shape[0]
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    if ws is None:
+        ws = torch.empty((max(convrot_dequant_workspace_size(N, K), 16),), dtype=torch.uint8, device=x.device)
+    _check("convrot_dequant_linear",
+           convrot_dequant_linear(x, M, K, wq, wbits, w_scale, N, group, y, ws, ws.numel()))
+    return y
 
 
 def workspace(M: int, K: int, device="cuda"):

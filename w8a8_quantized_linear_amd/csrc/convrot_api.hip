@@ -77,7 +77,7 @@ hipError_t launch_outs(const int8_t* xq, const float* xs, int wbits, int64_t M, 
 
 extern "C" {
 
-int convrot_version(void) { return 102; }
+int convrot_version(void) { return 103; }
 
 const char* convrot_status_string(int status) {
   switch (status) {
@@ -88,7 +88,7 @@ const char* convrot_status_string(int status) {
                                    "product)";
     case CONVROT_ERR_GROUP: return "group must be a power of two in [1, 256]";
     case CONVROT_ERR_ALIGN: return "tensor pointers must be 16-byte aligned (scales 4-byte aligned)";
-    case CONVROT_ERR_WORKSPACE: return "workspace smaller than convrot_workspace_size(M, K)";
+    case CONVROT_ERR_WORKSPACE: return "workspace smaller than the call's workspace size";
     case CONVROT_ERR_DEVICE: return "the HIP runtime reported an error";
     case CONVROT_ERR_DTYPE: return "unsupported weight dtype or bit width";
     case CONVROT_ERR_ARG: return "a scalar argument is out of range (eps negative or not finite, or n_outs "
@@ -202,6 +202,50 @@ int convrot_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* 
                         int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   return linear_impl(x, M, K, wq4, 4, w_scale, N, group, y, workspace, workspace_bytes, stream);
+}
+
+int convrot_dequantize_weight(const void* wq, int wbits, const float* w_scale, int64_t N, int64_t K, int group,
+                              uint16_t* w_out, hipStream_t stream) {
+  if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
+  if (int rc = check_k(K, group, wbits == 4)) return rc;
+  if (N < 0) return CONVROT_ERR_SHAPE;
+  if (N == 0) return CONVROT_OK;
+  if (!wq || !w_scale || !w_out) return CONVROT_ERR_NULL;
+  if (!aligned(wq, 16) || !aligned(w_out, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
+  return device_status(convrot::launch_dequantize_weight(wq, wbits, w_scale, N, K, log2_group(group), w_out, stream));
+}
+
+int convrot_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                      hipStream_t stream) {
+  if (M < 0 || N <= 0 || K <= 0 || K % 16 != 0 || K > CONVROT_MAX_K) return CONVROT_ERR_SHAPE;
+  if (M > kMaxRows || N > kMaxRows || !tiles_fit(M, (N + 127) / 128)) return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !w || !y) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return CONVROT_ERR_ALIGN;
+  return device_status(convrot::launch_gemm_bf16(x, w, M, N, K, y, stream));
+}
+
+size_t convrot_dequant_workspace_size(int64_t N, int64_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return round_up(size_t(N) * size_t(K) * 2, kAlign);
+}
+
+int convrot_dequant_linear(const uint16_t* x, int64_t M, int64_t K, const void* wq, int wbits,
+                           const float* w_scale, int64_t N, int group, uint16_t* y, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (wbits != 8 && wbits != 4) return CONVROT_ERR_DTYPE;
+  if (int rc = check_k(K, group, wbits == 4)) return rc;
+  if (M < 0 || N <= 0 || M > kMaxRows || N > kMaxRows || !tiles_fit(M, (N + 127) / 128))
+    return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !wq || !w_scale || !y || !workspace) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4) || !aligned(workspace, 16))
+    return CONVROT_ERR_ALIGN;
+  if (workspace_bytes < convrot_dequant_workspace_size(N, K)) return CONVROT_ERR_WORKSPACE;
+  uint16_t* w_hat = static_cast<uint16_t*>(workspace);
+  const hipError_t e = convrot::launch_dequantize_weight(wq, wbits, w_scale, N, K, log2_group(group), w_hat, stream);
+  if (e != hipSuccess) return CONVROT_ERR_DEVICE;
+  return device_status(convrot::launch_gemm_bf16(x, w_hat, M, N, K, y, stream));
 }
 
 int convrot_gemm_i8_multi(const int8_t* xq, const float* x_scale, int wbits, int64_t M, int64_t K,

@@ -42,6 +42,16 @@ hipError_t launch_rmsnorm_rotate_quant_g256(const uint16_t* x, const float* norm
 hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, int64_t K, int log2g,
                                      uint8_t* wq4, float* scale, int32_t* clip_index, hipStream_t stream);
 
+// Weight-only path: codes (int8 [rows, K] or packed int4 [rows, K/2]) and
+// row scales -> the un-rotated weight as bf16 [rows, K].
+hipError_t launch_dequantize_weight(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
+                                    int log2g, uint16_t* out, hipStream_t stream);
+
+// y = bf16(x . w^T) for bf16 x [M, K] and w [N, K], fp32 accumulation
+// (the matmul of the weight-only path).
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                            hipStream_t stream);
+
 // One weight matrix of a GEMM launch and its outputs (row stride ldy
 // elements); acc and y may each be null, the same way for every output.
 struct GemmOutDesc {

@@ -62,6 +62,8 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
@@ -166,12 +168,14 @@ struct CfgK {
   static constexpr bool PERSIST = !(BM == 256 && BN == 256);
 };
 
-template <int BM, int BN, bool W4, bool EVEN, bool MULTI>
+template <int BM, int BN, bool W4, bool EVEN, bool MULTI, bool BF>
 __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx, int M,
                                                int K, int tiles_m, int tiles_n, const GemmOuts& outs) {
   using C = CfgK<BM, BN, W4>;
   constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS, P2 = C::P2;
-  const int Kb = W4 ? K / 2 : K;  // bytes per weight row
+  // K counts bytes of a token row (a bf16 row of k values is 2k bytes);
+  // Kb is the bytes of a weight row.
+  const int Kb = W4 ? K / 2 : K;
   // Separate arrays per stage buffer: the compiler then knows that the
   // global->LDS writes into one buffer do not alias reads of the other and
   // keeps them interleaved.
@@ -346,13 +350,18 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     for (int j = 0; j < TJ; ++j) fb[b][j] = *reinterpret_cast<const v4i*>(bx + (xadr[j] ^ xslice(sl)));
   };
 
-  v16i acc[TI][TJ];
+  using AccT = std::conditional_t<BF, v16f, v16i>;
+  AccT acc[TI][TJ];
   auto mfma = [&](int b) {
 #pragma unroll
     for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
+        if constexpr (BF)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[b][i]),
+                                                              __builtin_bit_cast(v8bf, fb[b][j]), acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
   };
   auto sync_stage = [&]() {
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0), vmcnt/expcnt untouched
@@ -381,7 +390,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // The tile's weight-row and token scales go to LDS with one 1 KB load each
   // (waves 0 and 1); they are first read in the epilogue.
   auto load_scales = [&]() {
-    if (has_y && wave < 2) {
+    if (!BF && has_y && wave < 2) {
       const float* src = wave == 0 ? sw + n0 : sx + m0;
       const int nrec = 4 * (wave == 0 ? rows_w : rows_x);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
@@ -463,7 +472,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
       const int N = outs.o[eo].N, ldy = outs.o[eo].ldy;
       int32_t* const acc_out = outs.o[eo].acc;
       uint16_t* const y = outs.o[eo].y;
-    if (has_acc) {
+    if constexpr (!BF) if (has_acc) {
       const bool vec_ok = ((N | ldy) & 3) == 0;
   #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -498,28 +507,39 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         // All scales this lane needs, read once: the staging writes below go
         // through a per-wave pointer the compiler cannot separate from the
         // scale arrays, so reads inside the block loop would be repeated.
+        // (The bf16 product has no scales.)
         float4 sw4s[TI][4];
         float sxv[TJ];
+        if constexpr (!BF) {
 #pragma unroll
-        for (int i = 0; i < TI; ++i)
+          for (int i = 0; i < TI; ++i)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + wn * WN + 4 * half + i * 32 + 8 * g);
+            for (int g = 0; g < 4; ++g)
+              sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + wn * WN + 4 * half + i * 32 + 8 * g);
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * WM + j * 32 + row];
+          for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * WM + j * 32 + row];
+        }
     #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const float sxj = sxv[j];
+        const float sxj = BF ? 0.f : sxv[j];
     #pragma unroll
         for (int i = 0; i < TI; ++i)
     #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const float4 sw4 = sw4s[i][g];
-            constexpr int sh = W4 ? 4 : 0;
-            const float f0 = (float(acc[i][j][4 * g + 0] >> sh) * sxj) * sw4.x;
-            const float f1 = (float(acc[i][j][4 * g + 1] >> sh) * sxj) * sw4.y;
-            const float f2 = (float(acc[i][j][4 * g + 2] >> sh) * sxj) * sw4.z;
-            const float f3 = (float(acc[i][j][4 * g + 3] >> sh) * sxj) * sw4.w;
+            float f0, f1, f2, f3;
+            if constexpr (BF) {
+              f0 = acc[i][j][4 * g + 0];
+              f1 = acc[i][j][4 * g + 1];
+              f2 = acc[i][j][4 * g + 2];
+              f3 = acc[i][j][4 * g + 3];
+            } else {
+              const float4 sw4 = sw4s[i][g];
+              constexpr int sh = W4 ? 4 : 0;
+              f0 = (float(acc[i][j][4 * g + 0] >> sh) * sxj) * sw4.x;
+              f1 = (float(acc[i][j][4 * g + 1] >> sh) * sxj) * sw4.y;
+              f2 = (float(acc[i][j][4 * g + 2] >> sh) * sxj) * sw4.z;
+              f3 = (float(acc[i][j][4 * g + 3] >> sh) * sxj) * sw4.w;
+            }
             const int q = i * 4 + g;
             *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * chunk_of(row, q) + 8 * half) =
                 make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
@@ -579,7 +599,7 @@ template <int BM, int BN, bool W4, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_kernel(const int8_t* __restrict__ X,
                                                                    const float* __restrict__ sx, int M, int K,
                                                                    int tiles_m, int tiles_n, GemmOuts outs) {
-  gemm_k128_body<BM, BN, W4, true, MULTI>(X, sx, M, K, tiles_m, tiles_n, outs);
+  gemm_k128_body<BM, BN, W4, true, MULTI, false>(X, sx, M, K, tiles_m, tiles_n, outs);
 }
 
 // Any K (a multiple of 16, of 32 for int4 weights): every chunk range-checked.
@@ -587,7 +607,17 @@ template <int BM, int BN, bool W4, bool MULTI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const int8_t* __restrict__ X,
                                                                         const float* __restrict__ sx, int M, int K,
                                                                         int tiles_m, int tiles_n, GemmOuts outs) {
-  gemm_k128_body<BM, BN, W4, false, MULTI>(X, sx, M, K, tiles_m, tiles_n, outs);
+  gemm_k128_body<BM, BN, W4, false, MULTI, false>(X, sx, M, K, tiles_m, tiles_n, outs);
+}
+
+// bf16 x bf16 -> fp32 on the same pipeline (the weight-only path's matmul):
+// a stage still moves 128 bytes of every row, i.e. 64 K values, and each
+// MFMA (v_mfma_f32_32x32x16_bf16) takes the same 16 bytes per lane per
+// operand as the int8 one.  K here counts row BYTES.
+template <int BM, int BN, bool EVEN>
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t* __restrict__ X, int M, int K,
+                                                                    int tiles_m, int tiles_n, GemmOuts outs) {
+  gemm_k128_body<BM, BN, false, EVEN, false, true>(X, nullptr, M, K, tiles_m, tiles_n, outs);
 }
 
 // Workgroups of `kernel` the current device runs at once: compute units x
@@ -758,7 +788,41 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
   return launch_tile<W4>(forced.bm ? forced : choose_tile(M, d, n), xq, x_scale, M, K, d, n, stream);
 }
 
+template <int BM, int BN>
+hipError_t launch_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K, uint16_t* y, hipStream_t stream) {
+  GemmOuts outs{};
+  outs.n = 1;
+  outs.o[0] = {reinterpret_cast<const uint8_t*>(w), nullptr, nullptr, y, N, N};
+  for (int o = 0; o < kMaxOuts; ++o) outs.tn0[o] = o ? INT_MAX : 0;
+  const int kbytes = 2 * K;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  using Kernel = void (*)(const int8_t*, int, int, int, int, GemmOuts);
+  const Kernel kernel = kbytes % 256 == 0 ? gemm_bf16_k64_kernel<BM, BN, true> : gemm_bf16_k64_kernel<BM, BN, false>;
+  const int64_t tiles = int64_t(tiles_m) * tiles_n;
+  int64_t slots = tiles;
+  if (CfgK<BM, BN, false>::PERSIST) {
+    slots = resident_slots(reinterpret_cast<const void*>(kernel));
+    if (slots <= 0) return hipErrorInvalidDeviceFunction;
+  }
+  const dim3 grid(unsigned(tiles < slots ? tiles : slots));
+  hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, reinterpret_cast<const int8_t*>(x), M, kbytes,
+                     tiles_m, tiles_n, outs);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                            hipStream_t stream) {
+  const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
+  const TileChoice forced = tile_override();
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, &d, 1);
+  if (tc.bm == 256 && tc.bn == 256) return launch_bf16<256, 256>(x, w, int(M), int(N), int(K), y, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_bf16<256, 192>(x, w, int(M), int(N), int(K), y, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128>(x, w, int(M), int(N), int(K), y, stream);
+  if (tc.bm == 128 && tc.bn == 256) return launch_bf16<128, 256>(x, w, int(M), int(N), int(K), y, stream);
+  return launch_bf16<128, 128>(x, w, int(M), int(N), int(K), y, stream);
+}
 
 hipError_t launch_gemm(const int8_t* xq, const float* x_scale, const void* wq, int wbits, const float* w_scale,
                        int64_t M, int64_t N, int64_t K, int32_t* acc_out, uint16_t* y, hipStream_t stream) {

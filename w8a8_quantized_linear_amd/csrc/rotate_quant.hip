@@ -327,7 +327,114 @@ hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* cod
   return hipGetLastError();
 }
 
+// Weight-only path: undo the rotation of a stored row.  Codes (int8, or
+// packed int4 with the low nibble first) are exact in fp32, and so is their
+// unnormalised transform t (|t| <= 256 * 128); the value is then
+// s_w * (t * 2^-(log2g/2)) with one rounding for even log2(g) (the power of
+// two is exact), or (t / sqrt(g)) * s_w for odd log2(g), and is rounded to
+// bf16.  ("MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file
+// table row "Matmul": the weight can be dequantized for a bf16 matmul.)
+template <int TPT, int C, bool W4>
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const void* __restrict__ wq,
+                                                           const float* __restrict__ w_scale, int64_t rows,
+                                                           int64_t K, int log2g, float inv_sqrt_g, float pow2_norm,
+                                                           uint16_t* __restrict__ out) {
+  constexpr int P = kThreads / TPT;
+  const int t = threadIdx.x % TPT;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = int64_t(blockIdx.x) * P + threadIdx.x / TPT;
+  const bool row_ok = row < rows;
+  const int64_t nchunks = K / 16;
+  const bool odd = (log2g & 1) != 0;
+
+  float v[C][16];
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    const int64_t c = t + int64_t(TPT) * j;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[j][i] = 0.f;
+    if (row_ok && c < nchunks) {
+      if constexpr (W4) {
+        const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(wq) + row * (K / 2) + c * 8);
+        const uint32_t w[2] = {b.x, b.y};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int nib = int((w[i / 8] >> (4 * (i % 8))) & 0xfu);
+          v[j][i] = float(nib >= 8 ? nib - 16 : nib);
+        }
+      } else {
+        const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(wq) + row * K + c * 16);
+        const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[j][i] = float(int8_t(w[i / 4] >> (8 * (i % 4))));
+      }
+    }
+  }
+  const float s = row_ok ? w_scale[row] : 0.f;
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    fwht_in_register(v[j], log2g);
+    fwht_cross_lane(v[j], log2g, lane);
+    const int64_t c = t + int64_t(TPT) * j;
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float a = odd ? (v[j][2 * i] * inv_sqrt_g) * s : s * (v[j][2 * i] * pow2_norm);
+      const float b = odd ? (v[j][2 * i + 1] * inv_sqrt_g) * s : s * (v[j][2 * i + 1] * pow2_norm);
+      o[i] = pack_bf16x2(a, b);
+    }
+    if (row_ok && c < nchunks) {
+      uint4* dst = reinterpret_cast<uint4*>(out + row * K + c * 16);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+template <bool W4>
+hipError_t dispatch_dequant(const void* wq, const float* w_scale, int64_t rows, int64_t K, int log2g,
+                            uint16_t* out, hipStream_t stream) {
+  const int64_t nchunks = K / 16;
+  const float inv_sqrt_g = float(1.0 / sqrt(double(1 << log2g)));
+  const float pow2_norm = (log2g & 1) ? 1.0f : ldexpf(1.0f, -(log2g / 2));
+  int tpt = 256, c = 1;
+  if (nchunks <= 256) {
+    tpt = 16;
+    while (tpt < nchunks) tpt *= 2;
+  } else {
+    c = int((nchunks + 255) / 256);
+  }
+  const int per_block = kThreads / tpt;
+  const dim3 grid(unsigned((rows + per_block - 1) / per_block));
+#define CONVROT_DQ(TPT_, C_)                                                                            \
+  hipLaunchKernelGGL((dequant_kernel<TPT_, C_, W4>), grid, dim3(kThreads), 0, stream, wq, w_scale, rows, K, \
+                     log2g, inv_sqrt_g, pow2_norm, out)
+  switch (tpt * 16 + c) {
+    case 16 * 16 + 1: CONVROT_DQ(16, 1); break;
+    case 32 * 16 + 1: CONVROT_DQ(32, 1); break;
+    case 64 * 16 + 1: CONVROT_DQ(64, 1); break;
+    case 128 * 16 + 1: CONVROT_DQ(128, 1); break;
+    case 256 * 16 + 1: CONVROT_DQ(256, 1); break;
+    case 256 * 16 + 2: CONVROT_DQ(256, 2); break;
+    case 256 * 16 + 3: CONVROT_DQ(256, 3); break;
+    case 256 * 16 + 4: CONVROT_DQ(256, 4); break;
+    case 256 * 16 + 5: CONVROT_DQ(256, 5); break;
+    case 256 * 16 + 6: CONVROT_DQ(256, 6); break;
+    case 256 * 16 + 7: CONVROT_DQ(256, 7); break;
+    case 256 * 16 + 8: CONVROT_DQ(256, 8); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef CONVROT_DQ
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_dequantize_weight(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
+                                    int log2g, uint16_t* out, hipStream_t stream) {
+  if (wbits == 4) return dispatch_dequant<true>(wq, w_scale, rows, K, log2g, out, stream);
+  return dispatch_dequant<false>(wq, w_scale, rows, K, log2g, out, stream);
+}
 
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g, int8_t* codes,
                                float* scale, hipStream_t stream) {
