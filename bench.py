@@ -16,7 +16,8 @@ with the preceding RMSNorm), and the CPU oracle timed on a bounded sample on
 this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--no-extras] [--profile {gemm,rq,rq_large,rmsnorm_rq,copy,linear}]
+                       [--no-extras]
+                       [--profile {gemm,gemm_bf16,rq,rq_large,rmsnorm_rq,copy,linear}]
 """
 from __future__ import annotations
 
@@ -34,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, ops/s * 1e-12
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 M, K, N, GROUP = 2048, 4096, 12288, 256
 
@@ -246,6 +248,43 @@ def extras_stack(torch, cr, wl, timer):
     return res
 
 
+def extras_dequant(torch, cr, wl, timer):
+    """Weight-only (dequant) path at the headline shape: the bf16 GEMM with
+    the dequantized weight resident, the dequantize kernel alone, and both
+    (convrot_dequant_linear); torch's bf16 matmul (the vendor library) on the
+    same buffers for context.  Operands cycle past 2x the MALL."""
+    dev = torch.device("cuda")
+    per = 2 * (M * K + N * K + M * N)
+    n = max(2, -(-2 * MALL_BYTES // per) + 1)
+    g = torch.Generator(device=dev).manual_seed(77)
+    xs = [torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
+    wqs, wss = [], []
+    for i in range(n):
+        w = torch.randn((N, K), generator=g, device=dev) * 0.02
+        wq, wsc = cr.quantize_weight(w)
+        wqs.append(wq)
+        wss.append(wsc)
+        del w
+    whs = [cr.dequantize_weight(wqs[i], wss[i], K) for i in range(n)]
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(n)]
+    wsp = torch.empty((cr.convrot_dequant_workspace_size(N, K),), dtype=torch.uint8, device=dev)
+    flops = 2.0 * M * N * K
+    t_g = timer.time(lambda i: cr.gemm_bf16(xs[i % n], whs[i % n], out=ys[i % n]), 50)
+    t_d = timer.time(lambda i: cr.convrot_dequantize_weight(wqs[i % n], 8, wss[i % n], N, K, GROUP, whs[i % n]), 50)
+    t_l = timer.time(lambda i: cr.dequant_linear(xs[i % n], wqs[i % n], wss[i % n], out=ys[i % n], ws=wsp), 50)
+    t_t = timer.time(lambda i: torch.matmul(xs[i % n], whs[i % n].t(), out=ys[i % n]), 50)
+    dq_bytes = N * K + 4 * N + 2 * N * K
+    res = {"workload": "weight-only path, M=2048 K=4096 N=12288 (bf16 activations, int8 weights dequantized to bf16)",
+           "gemm_bf16": {"us": round(t_g * 1e6, 2), "tflops": round(flops / t_g / 1e12, 1),
+                         "frac": round(flops / t_g / 1e12 / PEAK_BF16_TFLOPS, 4), "peak": PEAK_BF16_TFLOPS},
+           "dequantize_weight": {"us": round(t_d * 1e6, 2), "bytes": dq_bytes,
+                                 "achieved_gbs": round(dq_bytes / t_d / 1e9, 1)},
+           "dequant_linear": {"us": round(t_l * 1e6, 2), "tflops": round(flops / t_l / 1e12, 1)},
+           "torch_matmul_bf16": {"us": round(t_t * 1e6, 2), "tflops": round(flops / t_t / 1e12, 1)}}
+    del xs, wqs, wss, whs, ys, wsp
+    return res
+
+
 def rq_passes(torch, cr, timer):
     """Rotate-quantize bandwidth on the large passes, each cycled through
     enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16)."""
@@ -327,6 +366,16 @@ def profile_mode(mode, torch, cr, wl):
         torch.cuda.synchronize()
         log(f"profile mode rq_large M={m} K={k}: 3 launches")
         return
+    if mode == "gemm_bf16":
+        g = torch.Generator(device=dev).manual_seed(5)
+        xb = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+        wb = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            cr.gemm_bf16(xb, wb, out=yb)
+        torch.cuda.synchronize()
+        log(f"profile mode gemm_bf16 M={M} K={K} N={N}: 3 launches")
+        return
     if mode == "rmsnorm_rq":
         m, k = RMSNORM_PASS
         xd = torch.randn((m, k), device=dev).to(torch.bfloat16)
@@ -359,7 +408,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "rq", "rq_large", "rmsnorm_rq", "copy", "linear"], default=None)
+    ap.add_argument("--profile", choices=["gemm", "gemm_bf16", "rq", "rq_large", "rmsnorm_rq", "copy", "linear"], default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -478,6 +527,8 @@ def main():
     if not args.no_extras:
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
+        log("extras: weight-only path M=2048 K=4096 N=12288")
+        out["dequant_path"] = extras_dequant(torch, cr, wl, timer)
         log("extras: 32-layer stack M=8704")
         out["stack"] = extras_stack(torch, cr, wl, timer)
     if not args.no_cpu_baseline:
