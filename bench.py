@@ -285,6 +285,44 @@ def extras_dequant(torch, cr, wl, timer):
     return res
 
 
+def extras_vision(torch, cr, wl, timer):
+    """Group-16 linears of a ConvRot vision block (widths 1152 and 4304 are
+    not multiples of 256): qkv 1152->3456, proj 1152->1152, fc1 1152->4304,
+    fc2 4304->1152 at M=4096 patches, each with its own group-16
+    rotate-quantize; plus the group-16 rotate-quantize alone at M=16384."""
+    dev = torch.device("cuda")
+    Mv = 4096
+    lins = (("qkv", 1152, 3456), ("proj", 1152, 1152), ("fc1", 1152, 4304), ("fc2", 4304, 1152))
+    g = torch.Generator(device=dev).manual_seed(16)
+    acts = {k: torch.randn((Mv, k), generator=g, device=dev).to(torch.bfloat16) for k in (1152, 4304)}
+    ws_, outs = [], []
+    for name, k, n in lins:
+        w = torch.randn((n, k), generator=g, device=dev) * 0.02
+        ws_.append(cr.quantize_weight(w, group=16))
+        outs.append(torch.empty((Mv, n), dtype=torch.bfloat16, device=dev))
+    wsp = cr.workspace(Mv, 4304, dev)
+    ops = sum(2.0 * Mv * k * n for _, k, n in lins)
+
+    def block(_):
+        for (name, k, n), (wq, wsc), y in zip(lins, ws_, outs):
+            cr.w8a8_linear(acts[k], wq, wsc, group=16, out=y, ws=wsp)
+
+    t_b = timer.time(block, 30)
+    Mr, Kr = 16384, 4304
+    per = Mr * (3 * Kr + 4)
+    n = max(2, -(-2 * MALL_BYTES // per) + 1)
+    xs = [torch.randn((Mr, Kr), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
+    qs = [torch.empty((Mr, Kr), dtype=torch.int8, device=dev) for _ in range(n)]
+    ss = [torch.empty((Mr,), dtype=torch.float32, device=dev) for _ in range(n)]
+    t_r = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], Mr, Kr, 16, qs[i % n], ss[i % n]), 60)
+    res = {"workload": "vision block linears, group 16, M=4096 patches (qkv, proj, fc1, fc2)",
+           "us_per_block": round(t_b * 1e6, 1), "tops": round(ops / t_b / 1e12, 1),
+           "rotate_quant_g16": {"M": Mr, "K": Kr, "us": round(t_r * 1e6, 2), "bytes": per,
+                                "achieved_gbs": round(per / t_r / 1e9, 1)}}
+    del xs, qs, ss, acts, ws_, outs, wsp
+    return res
+
+
 def rq_passes(torch, cr, timer):
     """Rotate-quantize bandwidth on the large passes, each cycled through
     enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16)."""
@@ -529,6 +567,8 @@ def main():
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
         log("extras: weight-only path M=2048 K=4096 N=12288")
         out["dequant_path"] = extras_dequant(torch, cr, wl, timer)
+        log("extras: vision block, group 16")
+        out["vision_g16"] = extras_vision(torch, cr, wl, timer)
         log("extras: 32-layer stack M=8704")
         out["stack"] = extras_stack(torch, cr, wl, timer)
     if not args.no_cpu_baseline:

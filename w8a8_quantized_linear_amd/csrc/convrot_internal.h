@@ -26,6 +26,11 @@ hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_
 hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* x_scale,
                                     hipStream_t stream);
 
+// Fast path for bf16 activations with group 16 or 1 (log2g 4 or 0) and
+// K <= 8192; returns hipErrorNotSupported without launching otherwise.
+hipError_t launch_rotate_quant_small(const uint16_t* x, int64_t M, int64_t K, int log2g, int8_t* xq, float* x_scale,
+                                     hipStream_t stream);
+
 // RMSNorm with (1 + w) weights, then the activation rotate-and-quantize of
 // its bf16 output (bf16 input only).  y_norm, if not null, receives the
 // normalised bf16 row.

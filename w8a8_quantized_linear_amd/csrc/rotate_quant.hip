@@ -443,6 +443,11 @@ hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_
         launch_rotate_quant_g256(static_cast<const uint16_t*>(x), rows, K, codes, scale, stream);
     if (e != hipErrorNotSupported) return e;
   }
+  if (in_dtype == IN_BF16 && (log2g == 4 || log2g == 0)) {
+    const hipError_t e =
+        launch_rotate_quant_small(static_cast<const uint16_t*>(x), rows, K, log2g, codes, scale, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (in_dtype == IN_BF16) return dispatch<IN_BF16, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
   return dispatch<IN_F32, MODE_I8>(x, rows, K, log2g, codes, scale, nullptr, stream);
 }

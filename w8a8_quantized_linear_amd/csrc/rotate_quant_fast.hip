@@ -31,6 +31,8 @@
 // (tests/host/quotient_identities.c).
 #include "convrot_internal.h"
 
+#include <cstdlib>
+
 namespace convrot {
 namespace {
 
@@ -346,7 +348,188 @@ hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small groups (G = 16, the group size of ConvRot vision layers whose widths,
+// 1152 and 4304, are not multiples of 256: "qwen3vl_8b_int8_convrot", "Layer
+// and group selection"; and G = 1, plain row-wise int8).  A group is one
+// lane's chunk of 16 values, so the transform never leaves the lane: the
+// bit-0 butterfly fused with the unpack, then bits 1..3.  A row spreads over
+// L = 64 / RPW lanes of a wave (RPW rows per wave), lane l taking chunks
+// l, l + L, ..., so any multiple of 16 fits; RPW is chosen per K to waste
+// the fewest chunk slots.  Quantization is the group-256 kernel's (exact
+// quotient, half away from zero, tiny-row lift); 1/sqrt(16) = 1/4 is folded
+// into the scale.
+template <int G, int C, int RPW>
+__global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                      int K, int8_t* __restrict__ xq,
+                                                                      float* __restrict__ x_scale) {
+  static_assert(G == 1 || G == 16, "group");
+  constexpr int L = 64 / RPW;               // lanes per row
+  constexpr int P = kWaves * RPW;           // rows per workgroup iteration
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l = lane % L;
+  const int slot = wave * RPW + lane / L;   // this lane's row within the iteration
+  const int nchunks = K / 16;
+  const int64_t ngroups = (M + P - 1) / P;
+
+  u32x4 raw[C][2];
+  auto load = [&](int64_t tok) {
+    if (tok < M) {
+      const uint16_t* row = x + tok * K;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const int c = l + L * j;
+        if (c < nchunks) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(row + c * 16);
+          raw[j][0] = __builtin_nontemporal_load(p);
+          raw[j][1] = __builtin_nontemporal_load(p + 1);
+        } else {
+          raw[j][0] = u32x4{0u, 0u, 0u, 0u};
+          raw[j][1] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    }
+  };
+
+  int64_t grp = blockIdx.x;
+  load(grp * P + slot);
+  for (; grp < ngroups; grp += gridDim.x) {
+    const int64_t tok = grp * P + slot;
+    float v[C][16];
+#pragma unroll
+    for (int j = 0; j < C; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w = raw[j][i / 4][i % 4];
+        const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+        v[j][2 * i] = G == 16 ? lo + hi : lo;
+        v[j][2 * i + 1] = G == 16 ? lo - hi : hi;
+      }
+    load((grp + gridDim.x) * P + slot);
+
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if constexpr (G == 16) fwht16_rest(v[j]);
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) max3_abs(amax, v[j][i], v[j][i + 1]);
+    }
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+    float s = amax / 127.0f;                      // scale of the unnormalised values
+    float out_mul = G == 16 ? 0.25f : 1.0f;       // 1/sqrt(G), exact
+    if (s < 0x1p-100f && s > 0.f) {
+      // Tiny row (uniform over the row's lanes): lift by 2^64 as in the
+      // group-256 kernel so 1/s stays finite and the quotient identity holds.
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[j][i] *= 0x1p64f;
+      s = (amax * 0x1p64f) / 127.0f;
+      out_mul *= 0x1p-64f;
+    }
+    const float r = s > 0.f ? 1.0f / s : 0.f;
+    if (tok < M) {
+      if (l == 0) x_scale[tok] = s * out_mul;
+      int8_t* out = xq + tok * K;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        const int c = l + L * j;
+        if (c < nchunks) {
+          int q[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) q[i] = quantize(v[j][i], s, r);
+          const u32x4 o = {pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
+                           pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + c * 16));
+        }
+      }
+    }
+  }
+}
+
+template <int G, int C, int RPW>
+hipError_t launch_small(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, hipStream_t stream) {
+  constexpr int P = kWaves * RPW;
+  const int64_t ngroups = (M + P - 1) / P;
+  const int64_t max_blocks = 256 * 8;
+  const unsigned grid = unsigned(ngroups < max_blocks ? ngroups : max_blocks);
+  hipLaunchKernelGGL((rotate_quant_small_kernel<G, C, RPW>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K),
+                     xq, xs);
+  return hipGetLastError();
+}
+
+// Rows per wave and chunks per lane for K: the fewest empty chunk slots
+// (ties to more lanes per row), up to 8 chunks per lane (K <= 8192).  The
+// kernel times of the three choices differ by at most ~25 % (kernel trace,
+// K 1152 and 4304, M 1024 to 16384).
+template <int G>
+hipError_t launch_small_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, hipStream_t stream) {
+  const int64_t nch = K / 16;
+  int best_rpw = 0, best_c = 0;
+  int64_t best_waste = 0;
+  for (int rpw = 1; rpw <= 4; rpw *= 2) {
+    const int64_t lanes = 64 / rpw, c = (nch + lanes - 1) / lanes;
+    if (c > 8) continue;
+    const int64_t waste = (c * lanes - nch) * rpw;  // empty chunk slots per wave
+    if (best_rpw == 0 || waste < best_waste) {
+      best_waste = waste;
+      best_rpw = rpw;
+      best_c = int(c);
+    }
+  }
+  if (best_rpw == 0) return hipErrorNotSupported;
+  // Few rows: fewer rows per wave gives more, shorter waves (measured at
+  // K 1152: M 1024 3.9 against 5.0 us, M 4096 6.0 against 6.2 us); keep at
+  // least two waves per SIMD before packing rows.
+  while (best_rpw > 1 && M / best_rpw < 2048) {
+    const int rpw = best_rpw / 2;
+    const int64_t lanes = 64 / rpw, c = (nch + lanes - 1) / lanes;
+    if (c > 8) break;
+    best_rpw = rpw;
+    best_c = int(c);
+  }
+  // CONVROT_RQ_SMALL_RPW=<1|2|4> forces the rows per wave (a tuning override
+  // for sweeps; every choice gives identical results) when it fits.
+  static const int forced_rpw = [] {
+    const char* e = getenv("CONVROT_RQ_SMALL_RPW");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced_rpw == 1 || forced_rpw == 2 || forced_rpw == 4) {
+    const int64_t lanes = 64 / forced_rpw, c = (nch + lanes - 1) / lanes;
+    if (c <= 8) {
+      best_rpw = forced_rpw;
+      best_c = int(c);
+    }
+  }
+#define CONVROT_SMALL(RPW_)                                                        \
+  switch (best_c) {                                                                \
+    case 1: return launch_small<G, 1, RPW_>(x, M, K, xq, xs, stream);              \
+    case 2: return launch_small<G, 2, RPW_>(x, M, K, xq, xs, stream);              \
+    case 3: return launch_small<G, 3, RPW_>(x, M, K, xq, xs, stream);              \
+    case 4: return launch_small<G, 4, RPW_>(x, M, K, xq, xs, stream);              \
+    case 5: return launch_small<G, 5, RPW_>(x, M, K, xq, xs, stream);              \
+    case 6: return launch_small<G, 6, RPW_>(x, M, K, xq, xs, stream);              \
+    case 7: return launch_small<G, 7, RPW_>(x, M, K, xq, xs, stream);              \
+    default: return launch_small<G, 8, RPW_>(x, M, K, xq, xs, stream);             \
+  }
+  if (best_rpw == 1) CONVROT_SMALL(1)
+  if (best_rpw == 2) CONVROT_SMALL(2)
+  CONVROT_SMALL(4)
+#undef CONVROT_SMALL
+}
+
 }  // namespace
+
+// Group 16 or 1 (log2g 4 or 0), bf16 activations, K <= 8192; otherwise
+// hipErrorNotSupported without launching.
+hipError_t launch_rotate_quant_small(const uint16_t* x, int64_t M, int64_t K, int log2g, int8_t* xq, float* xs,
+                                     hipStream_t stream) {
+  if (log2g == 4) return launch_small_k<16>(x, M, K, xq, xs, stream);
+  if (log2g == 0) return launch_small_k<1>(x, M, K, xq, xs, stream);
+  return hipErrorNotSupported;
+}
 
 // Return hipErrorNotSupported (without launching) for shapes this path does
 // not cover; the caller then uses the general kernel.
