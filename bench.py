@@ -373,6 +373,27 @@ def rmsnorm_rq_pass(torch, cr, wl, timer):
     return res
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+
+
+def vendor_int_mm(torch, cr, wl, timer):
+    """torch._int_mm (the vendor library's int8 GEMM, int32 output; run only)
+    at the headline shape on cold operands, for context."""
+    dev = torch.device("cuda")
+    per = M * K + N * K + 4 * M * N
+    n = max(2, -(-2 * MALL_BYTES // per) + 1)
+    a = [torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev) for _ in range(n)]
+    b = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev).t().contiguous() for _ in range(n)]
+    c = [torch.empty((M, N), dtype=torch.int32, device=dev) for _ in range(n)]
+    t = timer.time(lambda i: torch._int_mm(a[i % n], b[i % n], out=c[i % n]), 50)
+    del a, b, c
+    return {"workload": "torch._int_mm int8 x int8 -> int32, M=2048 K=4096 N=12288 (no epilogue)",
+            "us": round(t * 1e6, 2), "tops": round(2.0 * M * N * K / t / 1e12, 1)}
+
+
 def copy_peak(torch, timer):
     """Measured device-to-device copy bandwidth (1 GiB, read + write bytes)."""
     a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
@@ -554,6 +575,7 @@ def main():
             "traffic": load_traffic("rotate_quant_C3u", RQ_SOURCES),
         },
         "parity_rel_l2_sampled": rel,
+        "device": device_info(torch),
     }
     log("rotate-quantize on the large passes")
     out["rotate_quant_large"] = {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -563,6 +585,11 @@ def main():
     log("fused RMSNorm + rotate-quantize M=8704 K=4096")
     out["rmsnorm_rotate_quant"] = rmsnorm_rq_pass(torch, cr, wl, timer)
     if not args.no_extras:
+        log("extras: vendor int8 GEMM for context")
+        try:
+            out["vendor_int_mm"] = vendor_int_mm(torch, cr, wl, timer)
+        except RuntimeError as e:  # not every torch build exposes an int8 GEMM
+            out["vendor_int_mm"] = {"error": str(e)[:200]}
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
         log("extras: weight-only path M=2048 K=4096 N=12288")
