@@ -466,6 +466,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     // needed between a block's staging writes and its reads, nor before the
     // next block overwrites the region: the next block's arithmetic overlaps
     // this block's LDS round trip and stores.
+    bool stores_counted = false;  // this epilogue issued exactly S_INT stores per wave
     {
       const int m0 = em0, n0 = en0;
       // This tile's output (set_tile above has moved on to the next tile).
@@ -504,6 +505,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         };
         // Interior tiles (and N a multiple of 8) store without per-element checks.
         const bool interior = m0 + BM <= M && n0 + BN <= N && ((N | ldy) & 7) == 0;
+        stores_counted = interior && !has_acc;
         // All scales this lane needs, read once: the staging writes below go
         // through a per-wave pointer the compiler cannot separate from the
         // scale arrays, so reads inside the block loop would be repeated.
@@ -579,16 +581,28 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
 
     // Next tile: its scales (this epilogue has finished reading the old ones),
     // the rest of its first loads, then wait until stage 0 has landed.
-    // Loads and stores retire in issue order, so at most the loads issued
-    // after stage 0 may still be outstanding.
+    // Vector memory operations retire in issue order, so it is enough that
+    // no more than the operations issued after stage 0 remain.  After an
+    // interior epilogue those are exactly its S_INT row stores (plus the
+    // stage-1 share), which need not drain before the next tile starts;
+    // after an edge tile (predicated stores) everything but the stage-1
+    // share is waited for.
+    constexpr int S_INT = TJ * (32 * NQ / 64);
+    static_assert(P2 + S_INT < 64, "vmcnt range");
     v = vn;
     sync_stage();
     load_scales();
     if constexpr (DEDICATED) {
-      wait_vmcnt<1>();
+      if (stores_counted)
+        wait_vmcnt<P2 + S_INT>();
+      else
+        wait_vmcnt<1>();
     } else {
       issue(1, 128, I0{}, IP2{});
-      wait_vmcnt<P2>();
+      if (stores_counted)
+        wait_vmcnt<P2 + S_INT>();
+      else
+        wait_vmcnt<P2>();
     }
     sync_stage();
   }
