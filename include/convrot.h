@@ -14,6 +14,10 @@
  *    convrot, convrot_groupsize 256, per_row, orig_dtype bfloat16.
  *  - "MossInt4", "Format": signed 4-bit weight codes two per byte with one
  *    F32 scale per row chosen by a clip search; 8-bit activations.
+ * Around that path the library also has: the RMSNorm that precedes the
+ * linears fused into the activation pass, several linears sharing one
+ * quantized input, the weight-only (dequant) path with a bf16 matmul, and
+ * small group sizes (16 for the vision widths, 1 for plain row-wise).
  *
  * Definitions used by every call (H is the Sylvester Hadamard matrix of
  * order g in natural order, H[i][j] = (-1)^popcount(i&j) / sqrt(g); a row is

@@ -7,6 +7,12 @@
 //   acc[m][n] = sum_k xq[m][k] * wq[n][k]           (both operands K-major)
 //   y[m][n]   = bf16_rne(((float)acc * x_scale[m]) * w_scale[n])
 //
+// The same body also serves (template flags) several weight matrices that
+// share one quantized input in one launch (MULTI), and the bf16 x bf16
+// matmul of the weight-only path (BF: v_mfma_f32_32x32x16_bf16, fp32
+// accumulators, y = bf16(acc)); the pipeline moves bytes, so both reuse it
+// unchanged.
+//
 // Tiling.  A 256-thread workgroup (4 waves, 2 x 2) computes a BM x BN output
 // tile (BM tokens x BN weight rows); each wave owns a (BM/2) x (BN/2)
 // sub-tile of 32x32 blocks accumulated by v_mfma_i32_32x32x32_i8.  The MFMA's
