@@ -17,7 +17,7 @@ this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-extras]
-                       [--profile {gemm,gemm_bf16,rq,rq_large,rmsnorm_rq,copy,linear}]
+                       [--profile {gemm,gemm_bf16,rq,rq_large,rq_g16,rmsnorm_rq,copy,linear}]
 """
 from __future__ import annotations
 
@@ -70,6 +70,8 @@ RQ_SOURCES = ["w8a8_quantized_linear_amd/csrc/rotate_quant.hip",
 RQ_PASSES = [(8704, 4096), (8704, 12288), (2048, 12288)]
 # The stack's RMSNorm input (hidden size 4096), normalised and quantized in one pass.
 RMSNORM_PASS = (8704, 4096)
+# A group-16 pass at the vision MLP width (4304 is not a multiple of 256).
+RQ_G16_PASS = (16384, 4304)
 
 
 def load_traffic(name, sources):
@@ -317,7 +319,7 @@ def extras_vision(torch, cr, wl, timer):
             cr.w8a8_linear(acts[k], wq, wsc, group=16, out=y, ws=wsp)
 
     t_b = timer.time(block, 30)
-    Mr, Kr = 16384, 4304
+    Mr, Kr = RQ_G16_PASS
     per = Mr * (3 * Kr + 4)
     n = max(2, -(-2 * MALL_BYTES // per) + 1)
     xs = [torch.randn((Mr, Kr), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
@@ -327,7 +329,9 @@ def extras_vision(torch, cr, wl, timer):
     res = {"workload": "vision block linears, group 16, M=4096 patches (qkv, proj, fc1, fc2)",
            "us_per_block": round(t_b * 1e6, 1), "tops": round(ops / t_b / 1e12, 1),
            "rotate_quant_g16": {"M": Mr, "K": Kr, "us": round(t_r * 1e6, 2), "bytes": per,
-                                "achieved_gbs": round(per / t_r / 1e9, 1)}}
+                                "achieved_gbs": round(per / t_r / 1e9, 1),
+                                "frac": round(per / t_r / 1e9 / PEAK_HBM_GBS, 4),
+                                "traffic": load_traffic("rotate_quant_g16_M16384_K4304", RQ_SOURCES)}}
     del xs, qs, ss, acts, ws_, outs, wsp
     return res
 
@@ -434,6 +438,16 @@ def profile_mode(mode, torch, cr, wl):
         torch.cuda.synchronize()
         log(f"profile mode rq_large M={m} K={k}: 3 launches")
         return
+    if mode == "rq_g16":
+        m, k = RQ_G16_PASS
+        xd = torch.randn((m, k), device=dev).to(torch.bfloat16)
+        xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+        xs = torch.empty((m,), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            cr.convrot_rotate_quant(xd, m, k, 16, xq, xs)
+        torch.cuda.synchronize()
+        log(f"profile mode rq_g16 M={m} K={k} group 16: 3 launches")
+        return
     if mode == "gemm_bf16":
         g = torch.Generator(device=dev).manual_seed(5)
         xb = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
@@ -476,7 +490,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "gemm_bf16", "rq", "rq_large", "rmsnorm_rq", "copy", "linear"], default=None)
+    ap.add_argument("--profile", choices=["gemm", "gemm_bf16", "rq", "rq_large", "rq_g16", "rmsnorm_rq", "copy", "linear"], default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
