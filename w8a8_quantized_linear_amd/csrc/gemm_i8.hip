@@ -651,7 +651,11 @@ int resident_slots(const void* kernel) {
     int device, slots;
   };
   static std::mutex mu;
-  static Entry cache[64];
+  // Room for every persistent kernel here (int8, int4, multi-output and
+  // bf16 variants: 40) on several devices; past that the answer is
+  // recomputed on each call, which is correct but slower.
+  constexpr int kEntries = 256;
+  static Entry cache[kEntries];
   static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -665,7 +669,7 @@ int resident_slots(const void* kernel) {
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
   const int slots = cus * (per_cu > 0 ? per_cu : 1);
   std::lock_guard<std::mutex> lock(mu);
-  if (used < 64) cache[used++] = {kernel, dev, slots};
+  if (used < kEntries) cache[used++] = {kernel, dev, slots};
   return slots;
 }
 
