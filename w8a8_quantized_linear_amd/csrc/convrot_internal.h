@@ -20,9 +20,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g,
                                int8_t* codes, float* scale, hipStream_t stream);
 
-// Fast path for bf16 activations with group 256 (K a multiple of 1024 up to
-// 16384, except 5, 7, 9..11, 13..15 x 1024); returns hipErrorNotSupported
-// without launching for other shapes.
+// Fast path for bf16 activations with group 256 (K a multiple of 256 up to
+// 16384); returns hipErrorNotSupported without launching for other shapes.
 hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* x_scale,
                                     hipStream_t stream);
 

@@ -142,6 +142,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
   const int64_t ngroups = (M + P - 1) / P;
   // element offset of chunk j of this lane inside a token row
   auto chunk_off = [&](int j) { return (j * (64 * TW) + wt * 64 + chunk_lane) * 16; };
+  // A row of K = 256 * G values fills G of the 4 * C * TW group slots
+  // (group of chunk j: (j * TW + wt) * 4 + lane / 16); the rest stay zero
+  // and are neither loaded nor stored.  Uniform over a 16-lane group.
+  const int nvalid = K >> 8;
+  auto slot_ok = [&](int j) { return ((j * TW + wt) * 4 + (lane >> 4)) < nvalid; };
 
   u32x4 raw[C][2];
   auto load = [&](int64_t tok) {
@@ -149,9 +154,14 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       const uint16_t* row = x + tok * K;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
-        const u32x4* p = reinterpret_cast<const u32x4*>(row + chunk_off(j));
-        raw[j][0] = __builtin_nontemporal_load(p);
-        raw[j][1] = __builtin_nontemporal_load(p + 1);
+        if (slot_ok(j)) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(row + chunk_off(j));
+          raw[j][0] = __builtin_nontemporal_load(p);
+          raw[j][1] = __builtin_nontemporal_load(p + 1);
+        } else {
+          raw[j][0] = u32x4{0u, 0u, 0u, 0u};
+          raw[j][1] = u32x4{0u, 0u, 0u, 0u};
+        }
       }
     }
   };
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       const int l = e & 63, q = (e >> 6) & 3, jt = e >> 8;
       const int lg = l & 15, lu = lg ^ ((lg & 4) ? 3 : 0);
       const int col = ((jt / TW) * (64 * TW) + (jt % TW) * 64 + (l & ~15) + lu) * 16 + 4 * q;
-      const float4 f = *reinterpret_cast<const float4*>(norm_w + col);
+      const float4 f = col < K ? *reinterpret_cast<const float4*>(norm_w + col) : make_float4(0.f, 0.f, 0.f, 0.f);
       w1s[e] = make_float4(1.0f + f.x, 1.0f + f.y, 1.0f + f.z, 1.0f + f.w);
     }
     __syncthreads();
@@ -182,7 +192,8 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
     for (int j = 0; j < C; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 f = *reinterpret_cast<const float4*>(norm_w + chunk_off(j) + 4 * q);
+        const float4 f = slot_ok(j) ? *reinterpret_cast<const float4*>(norm_w + chunk_off(j) + 4 * q)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
         w1r[j][4 * q + 0] = 1.0f + f.x;
         w1r[j][4 * q + 1] = 1.0f + f.y;
         w1r[j][4 * q + 2] = 1.0f + f.z;
@@ -249,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
             wd[j][i] = pack_bf16x2((lo * r) * w1[2 * h], (hi * r) * w1[2 * h + 1]);
           }
         }
-        if (y_norm != nullptr && tok < M) {
+        if (y_norm != nullptr && tok < M && slot_ok(j)) {
           u32x4* dst = reinterpret_cast<u32x4*>(y_norm + tok * K + chunk_off(j));
           dst[0] = u32x4{wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
           dst[1] = u32x4{wd[j][4], wd[j][5], wd[j][6], wd[j][7]};
@@ -308,6 +319,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       int8_t* out = xq + tok * K;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
+        if (!slot_ok(j)) continue;  // past the row's end
         int q[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) q[i] = quantize(v[j][i], ds, dr);
@@ -336,33 +348,34 @@ hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs
   return hipGetLastError();
 }
 
-template <bool NORM>
-hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w, float eps,
-                    uint16_t* y_norm, hipStream_t stream) {
-  if (K % 1024 != 0) return hipErrorNotSupported;
+template <int C, int TW, bool NORM>
+hipError_t launch_split(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w,
+                        float eps, uint16_t* y_norm, hipStream_t stream) {
   // Few tokens (under four waves per SIMD with one wave per token): split
   // each token over twice the waves, so the waves are shorter and more of
   // them hide each other's latency (kernel trace, K 4096: M 512 5.96 ->
   // 4.20 us, M 2048 8.40 -> 7.96 us; M 8704 is 4 % faster unsplit).
-  if (M < 4096) {
-    switch (K / 1024) {
-      case 2: return launch<1, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-      case 4: return launch<2, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-      case 8: return launch<2, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-      default: break;
-    }
+  if constexpr (C % 2 == 0 && TW < 4) {
+    if (M < 4096) return launch<C / 2, 2 * TW, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
   }
-  switch (K / 1024) {
-    case 1: return launch<1, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 2: return launch<2, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 3: return launch<3, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 4: return launch<4, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 6: return launch<3, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 8: return launch<4, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 12: return launch<3, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    case 16: return launch<4, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-    default: return hipErrorNotSupported;
-  }
+  return launch<C, TW, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+}
+
+// Any K = 256 * G up to 16384: the G groups take 4 * C * TW slots, with
+// one wave per token up to 16 groups, two up to 32, four up to 64.
+template <bool NORM>
+hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w, float eps,
+                    uint16_t* y_norm, hipStream_t stream) {
+  if (K % 256 != 0 || K > 16384) return hipErrorNotSupported;
+  const int G = int(K / 256);
+  if (G <= 4) return launch_split<1, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 8) return launch_split<2, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 12) return launch_split<3, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 16) return launch_split<4, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 24) return launch_split<3, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 32) return launch_split<4, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 48) return launch_split<3, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  return launch_split<4, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
 }
 
 // ---------------------------------------------------------------------------
