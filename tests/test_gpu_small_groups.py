@@ -84,3 +84,21 @@ def test_vision_linears_sampled(lib, name, K, N):
     wq_ref, ws_ref = oracle.quantize_weight_i8(w[rows], 16)
     y_ref = oracle.epilogue(oracle.gemm_i8(xq_ref, wq_ref), xs_ref, ws_ref)
     assert_rel_l2(y[np.ix_(toks, rows)], y_ref)
+
+
+def test_vision_w4a8_linear_sampled(lib):
+    """Packed int4 weights with group 16 at the vision MLP shape (K = 1152,
+    not a multiple of 256, so the GEMM takes its range-checked path)."""
+    import torch
+    M, K, N = 1024, 1152, 4304
+    say(f"vision W4A8 M={M} K={K} N={N} group 16")
+    x = wl.make_activations(M, K, K // 100, seed=77)
+    w = wl.make_weight(N, K, seed=78)
+    wq4, ws = lib.quantize_weight(torch.from_numpy(w).cuda(), group=16, bits=4)
+    y = bf16_from_dev(lib.w4a8_linear(bf16_to_dev(x), wq4, ws, group=16))
+    rng = np.random.default_rng(79)
+    toks = np.sort(rng.choice(M, 12, replace=False))
+    rows = np.sort(rng.choice(N, 96, replace=False))
+    packed_ref, ws_ref, _ = oracle.quantize_weight_i4(w[rows], 16)
+    y_ref = oracle.w4a8_linear(x[toks], packed_ref, ws_ref, 16)
+    assert_rel_l2(y[np.ix_(toks, rows)], y_ref)
