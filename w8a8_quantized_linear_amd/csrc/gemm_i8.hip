@@ -69,6 +69,15 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte output store marked nontemporal: the rows are streamed out and
+// not read again by this kernel, and keeping them out of the caches' way
+// measured 7-12 % faster on the large shapes (same-box A/B: M 2048 K 4096
+// N 12288 99.2 -> 92.2 us, M 8704 K 4096 N 12288 434.6 -> 384.6 us).
+__device__ __forceinline__ void store_nt(uint16_t* dst, const uint4& v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(dst));
+}
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -558,7 +567,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
             const int id = lane + 64 * k;
             const int r = id / NQ, q = id % NQ;
             const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
-            *reinterpret_cast<uint4*>(y + int64_t(m0 + wm * WM + j * 32 + r) * ldy + (n0 + wn * WN + 8 * q)) = v;
+            store_nt(y + int64_t(m0 + wm * WM + j * 32 + r) * ldy + (n0 + wn * WN + 8 * q), v);
           }
         } else {
     #pragma unroll
@@ -570,7 +579,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
             const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * chunk_of(r, q));
             if (m < M) {
               if (((N | ldy) & 7) == 0 && n + 7 < N) {
-                *reinterpret_cast<uint4*>(y + int64_t(m) * ldy + n) = v;
+                store_nt(y + int64_t(m) * ldy + n, v);
               } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     #pragma unroll
