@@ -82,6 +82,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kThreads = 256;
+constexpr int kGroupM = 4;  // M-tiles per block of the tile order
 constexpr unsigned kOOB = 0x7ffffff0u;  // buffer offset beyond every range: reads as zero
 constexpr int kBufFlags = 0x00020000;   // raw buffer descriptor word 3 (gfx9 family)
 
@@ -231,12 +232,28 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   __amdgpu_buffer_rsrc_t rsx, rsw;
   auto set_tile = [&](int v) {
     const int t = tile_of(v);
-    const int tn = t / tiles_m;
+    // Tile t in blocks of kGroupM M-tiles walked N-tile by N-tile, so an
+    // XCD's contiguous run of tiles (see tile_of) covers fewer token rows
+    // and re-reads less of X (same-box A/B against plain N-major order:
+    // M 8704 N 12288 -3.0 %, M 2048 K 12288 -1.9 %, others -0.2..-1.3 %).
+    int tm, tn;
+    {
+      const int nb = tiles_m / kGroupM, per_block = kGroupM * tiles_n, b = t / per_block;
+      if (b < nb) {
+        const int w = t - b * per_block;
+        tm = b * kGroupM + w % kGroupM;
+        tn = w / kGroupM;
+      } else {  // the last rows of M-tiles, fewer than kGroupM
+        const int h = tiles_m - nb * kGroupM, w = t - nb * per_block;
+        tm = nb * kGroupM + w % h;
+        tn = w / h;
+      }
+    }
     const int o = out_of(tn);
     cur = o;
     W = outs.o[o].W;
     sw = outs.o[o].sw;
-    m0 = (t % tiles_m) * BM;
+    m0 = tm * BM;
     n0 = (tn - (MULTI ? outs.tn0[o] : 0)) * BN;
     rows_x = min(BM, M - m0);
     rows_w = min(BN, outs.o[o].N - n0);
