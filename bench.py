@@ -158,8 +158,11 @@ def cpu_baseline(x, w, target_s=12.0):
     }
 
 
-def check_parity(torch, cr, x, w, y_dev):
-    """Sampled parity of the benchmarked output against the oracle."""
+def check_parity(torch, cr, x, w, y_dev, xq_dev, xs_dev, wq_dev, ws_dev):
+    """Sampled parity of the benchmarked buffers against the oracle, on 16
+    tokens x 128 weight rows: the activation and weight codes (fraction that
+    differ), the int32 accumulators of the GPU's own codes (exact or not)
+    and the bf16 output (relative L2)."""
     import oracle
     rng = np.random.default_rng(7)
     toks = np.sort(rng.choice(M, 16, replace=False))
@@ -169,7 +172,21 @@ def check_parity(torch, cr, x, w, y_dev):
     y_ref = oracle.epilogue(oracle.gemm_i8(xq, wq), xs, ws)
     y = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)[np.ix_(toks, rows)]
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    return float(np.linalg.norm(f(y) - f(y_ref)) / np.linalg.norm(f(y_ref)))
+    xq_g = xq_dev.cpu().numpy()[toks]
+    wq_g = wq_dev.cpu().numpy()[rows]
+    # The GEMM on the GPU's own codes, all N, accumulators kept.
+    acc = torch.empty((M, N), dtype=torch.int32, device=xq_dev.device)
+    _ok(cr, cr.convrot_gemm_i8(xq_dev, xs_dev, wq_dev, 8, ws_dev, M, N, K, acc, None))
+    torch.cuda.synchronize()
+    acc_g = acc.cpu().numpy()[np.ix_(toks, rows)]
+    del acc
+    return {
+        "sample": "16 tokens x 128 weight rows",
+        "rel_l2": float(np.linalg.norm(f(y) - f(y_ref)) / np.linalg.norm(f(y_ref))),
+        "code_mismatch_frac": float(np.mean(xq_g != xq)),
+        "weight_code_mismatch_frac": float(np.mean(wq_g != wq)),
+        "acc_exact": bool(np.array_equal(acc_g, oracle.gemm_i8(xq_g, wq_g))),
+    }
 
 
 def extras_w4a8(torch, cr, wl, timer):
@@ -556,8 +573,9 @@ def main():
     rq_bytes = M * (3 * K + 4)
     rq_gbs = rq_bytes / t_rq / 1e9
 
-    rel = check_parity(torch, cr, x, w, sets[(args.steps - 1) % nsets][3])
-    log(f"parity (sampled, vs oracle): rel L2 {rel:.2e}")
+    last = sets[(args.steps - 1) % nsets]
+    parity = check_parity(torch, cr, x, w, last[3], *q[(args.steps - 1) % nsets], last[1], last[2])
+    log(f"parity (sampled, vs oracle): {parity}")
 
     out = {
         "metric": "W8A8 ConvRot linear TOPS & tokens/s (M=2048,K=4096,N=12288); % int8 MFMA peak",
@@ -600,7 +618,7 @@ def main():
             "algorithmic_bytes_per_launch": rq_bytes,
             "traffic": load_traffic("rotate_quant_C3u", RQ_SOURCES),
         },
-        "parity_rel_l2_sampled": rel,
+        "parity": parity,
         "device": device_info(torch),
     }
     log("rotate-quantize on the large passes")
