@@ -767,12 +767,16 @@ struct Plan {
 // moves per MFMA, so the largest tile (256x256: fewest L2->LDS bytes per
 // operation) wins once it fills several whole rounds of the 256 CUs;
 // otherwise 256x192 when it fills at least three quarters of a round, and
-// 128x128 for small problems (more CUs busy).  Splitting N into bands of
+// 128x128 for small problems (more CUs busy).  With a short K (fewer than 16
+// stages of 128 bytes per token row) a tile's set-up and epilogue weigh as
+// much as its main loop, and 128x128 wins below the 256x256 case: two of its
+// workgroups share a CU and hide each other's (M 4096, K 1152, N 3456:
+// 31.6 -> 26.4 us against 256x192).  Splitting N into bands of
 // different tiles to even out a partial round measured no faster than a
 // single 256x192 launch (the second launch waits for the first).  With
 // several outputs the tiles of all of them count, and 256x256 needs every
 // output's N to be a multiple of 256.
-TileChoice choose_tile(int64_t M, const GemmOutDesc* d, int n) {
+TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   const int cus = 256;
   auto tiles = [&](int bm, int bn) {
     int64_t t = 0;
@@ -782,7 +786,7 @@ TileChoice choose_tile(int64_t M, const GemmOutDesc* d, int n) {
   bool n256 = true;
   for (int o = 0; o < n; ++o) n256 = n256 && d[o].N % 256 == 0;
   if (n256 && tiles(256, 256) >= 3 * cus) return {256, 256};
-  if (4 * tiles(256, 192) >= 3 * cus) return {256, 192};
+  if (ksteps >= 16 && 4 * tiles(256, 192) >= 3 * cus) return {256, 192};
   return {128, 128};
 }
 
@@ -835,7 +839,8 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     return hipSuccess;
   }
   const TileChoice forced = tile_override();
-  return launch_tile<W4>(forced.bm ? forced : choose_tile(M, d, n), xq, x_scale, M, K, d, n, stream);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
+  return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
 
 template <int BM, int BN>
@@ -866,7 +871,7 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t stream) {
   const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
   const TileChoice forced = tile_override();
-  const TileChoice tc = forced.bm ? forced : choose_tile(M, &d, 1);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1);
   if (tc.bm == 256 && tc.bn == 256) return launch_bf16<256, 256>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_bf16<256, 192>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128>(x, w, int(M), int(N), int(K), y, stream);
