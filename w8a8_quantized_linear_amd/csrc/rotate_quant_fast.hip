@@ -3,12 +3,11 @@
 // INT8 (W8A8, ConvRot)", file table rows "Quantized" and "Matmul").
 //
 // One token row is held in the registers of TW wavefronts (TW = 1 for
-// K <= 4096 when there are many tokens, more for longer rows or few
-// tokens); each lane owns C chunks of 16 consecutive bf16 values and a
+// short rows, more for longer rows or few tokens); each lane owns C chunks
+// of 16 consecutive bf16 values and a
 // group of 256 values lives in 16 consecutive lanes (one DPP row).  No LDS
-// and no barrier is needed when TW = 1.  A workgroup normally takes one
-// group of tokens; the loop over groups (each wave fetching its next row
-// while it transforms the current one) only serves grids past 2^30 groups.
+// and no barrier is needed when TW = 1.  A workgroup takes one group of
+// tokens; a launch covers at most 2^30 groups (larger M takes several).
 //
 // Walsh-Hadamard transform of a group (unnormalised; the 1/16 is a power of
 // two and is folded exactly into the scale):
@@ -139,7 +138,6 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
   const float c3 = (u & 8) ? -1.f : 1.f;
   const float sgn = c0 * c1 * c2 * c3;
 
-  const int64_t ngroups = (M + P - 1) / P;
   // element offset of chunk j of this lane inside a token row
   auto chunk_off = [&](int j) { return (j * (64 * TW) + wt * 64 + chunk_lane) * 16; };
   // A row of K = 256 * G values fills G of the 4 * C * TW group slots
@@ -201,10 +199,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       }
   }
 
-  int64_t grp = blockIdx.x;
-  load(grp * P + wave / TW);
-  for (; grp < ngroups; grp += gridDim.x) {
-    const int64_t tok = grp * P + wave / TW;
+  {
+    const int64_t tok = int64_t(blockIdx.x) * P + wave / TW;
+    load(tok);
     uint32_t wd[C][8];  // the row's bf16 pairs as loaded (or as normalised)
 #pragma unroll
     for (int j = 0; j < C; ++j)
@@ -213,8 +210,6 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
         wd[j][i] = raw[j][0][i];
         wd[j][4 + i] = raw[j][1][i];
       }
-    // prefetch the next token of this wave while transforming this one
-    load((grp + gridDim.x) * P + wave / TW);
 
     if constexpr (NORM) {
       // mean square in fp64 (each square of a bf16 value is exact there),
@@ -335,17 +330,21 @@ template <int C, int TW, bool NORM>
 hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w, float eps,
                   uint16_t* y_norm, hipStream_t stream) {
   constexpr int P = kWaves / TW;
-  const int64_t ngroups = (M + P - 1) / P;
   // One workgroup per group of tokens: the dispatcher then balances the
   // tail by itself (a persistent grid of 2048 workgroups left a partial
   // last round: kernel trace at M 8704, K 12288: 66.6 -> 61.8 us, M 30000,
-  // K 4096: 80.0 -> 74.8 us; the per-wave token loop only remains for
-  // more than 2^30 groups).
-  const int64_t max_blocks = int64_t(1) << 30;
-  const unsigned grid = unsigned(ngroups < max_blocks ? ngroups : max_blocks);
-  hipLaunchKernelGGL((rotate_quant_g256_kernel<C, TW, NORM>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K),
-                     xq, xs, norm_w, eps, y_norm);
-  return hipGetLastError();
+  // K 4096: 80.0 -> 74.8 us).  Without the per-wave token loop the kernel
+  // needs 30 fewer registers at C = 4 (same-box A/B, M 8704: K 8192
+  // 44.5 -> 40.5 us, K 12288 60.0 -> 57.5 us, K 4096 23.8 -> 23.4 us).
+  const int64_t rows_per_launch = (int64_t(1) << 30) * P;
+  for (int64_t m0 = 0; m0 < M; m0 += rows_per_launch) {
+    const int64_t mc = M - m0 < rows_per_launch ? M - m0 : rows_per_launch;
+    hipLaunchKernelGGL((rotate_quant_g256_kernel<C, TW, NORM>), dim3(unsigned((mc + P - 1) / P)), dim3(kThreads), 0,
+                       stream, x + m0 * K, mc, int(K), xq + m0 * K, xs + m0, norm_w, eps,
+                       y_norm ? y_norm + m0 * K : nullptr);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int C, int TW, bool NORM>
@@ -371,7 +370,17 @@ hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
   if (G <= 4) return launch_split<1, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
   if (G <= 8) return launch_split<2, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
   if (G <= 12) return launch_split<3, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
-  if (G <= 16) return launch_split<4, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  if (G <= 16) {
+    // The plain pass at K 4096 runs best with a token over several waves:
+    // four below 4096 tokens, two above (sweep of every (C, TW) at K 4096:
+    // M 2048 8.01 -> 7.55 us, M 8704 23.0 -> 21.7 us).  The fused norm pass
+    // is best as before.
+    if constexpr (!NORM) {
+      if (M < 4096) return launch<1, 4, false>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+      return launch<2, 2, false>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+    }
+    return launch_split<4, 1, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  }
   if (G <= 24) return launch_split<3, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
   if (G <= 32) return launch_split<4, 2, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
   if (G <= 48) return launch_split<3, 4, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
@@ -401,7 +410,6 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
   const int l = lane % L;
   const int slot = wave * RPW + lane / L;   // this lane's row within the iteration
   const int nchunks = K / 16;
-  const int64_t ngroups = (M + P - 1) / P;
 
   u32x4 raw[C][2];
   auto load = [&](int64_t tok) {
@@ -422,10 +430,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
     }
   };
 
-  int64_t grp = blockIdx.x;
-  load(grp * P + slot);
-  for (; grp < ngroups; grp += gridDim.x) {
-    const int64_t tok = grp * P + slot;
+  {
+    const int64_t tok = int64_t(blockIdx.x) * P + slot;
+    load(tok);
     float v[C][16];
 #pragma unroll
     for (int j = 0; j < C; ++j)
@@ -436,7 +443,6 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
         v[j][2 * i] = G == 16 ? lo + hi : lo;
         v[j][2 * i + 1] = G == 16 ? lo - hi : hi;
       }
-    load((grp + gridDim.x) * P + slot);
 
     float amax = 0.f;
 #pragma unroll
@@ -482,12 +488,14 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
 template <int G, int C, int RPW>
 hipError_t launch_small(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, hipStream_t stream) {
   constexpr int P = kWaves * RPW;
-  const int64_t ngroups = (M + P - 1) / P;
-  const int64_t max_blocks = int64_t(1) << 30;  // one workgroup per group, as above
-  const unsigned grid = unsigned(ngroups < max_blocks ? ngroups : max_blocks);
-  hipLaunchKernelGGL((rotate_quant_small_kernel<G, C, RPW>), dim3(grid), dim3(kThreads), 0, stream, x, M, int(K),
-                     xq, xs);
-  return hipGetLastError();
+  const int64_t rows_per_launch = (int64_t(1) << 30) * P;  // one workgroup per group, as above
+  for (int64_t m0 = 0; m0 < M; m0 += rows_per_launch) {
+    const int64_t mc = M - m0 < rows_per_launch ? M - m0 : rows_per_launch;
+    hipLaunchKernelGGL((rotate_quant_small_kernel<G, C, RPW>), dim3(unsigned((mc + P - 1) / P)), dim3(kThreads), 0,
+                       stream, x + m0 * K, mc, int(K), xq + m0 * K, xs + m0);
+    if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Rows per wave and chunks per lane for K: the fewest empty chunk slots
