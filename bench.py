@@ -94,11 +94,22 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def time(self, fn, reps, warm=3):
+    def time(self, fn, reps, warm=3, warm_s=0.05):
+        """Seconds per launch of fn over reps launches, after warm-up
+        launches for at least warm_s seconds: the device needs tens of
+        milliseconds of load to reach its steady clock (after an idle spell,
+        e.g. the host-side parity check, a pass timed at once measured up to
+        20 % slower)."""
         torch = self.torch
-        for i in range(warm):
-            fn(i)
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        i = 0
+        while True:
+            for _ in range(warm):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= warm_s:
+                break
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
         s.record()
@@ -342,7 +353,7 @@ def extras_vision(torch, cr, wl, timer):
     xs = [torch.randn((Mr, Kr), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
     qs = [torch.empty((Mr, Kr), dtype=torch.int8, device=dev) for _ in range(n)]
     ss = [torch.empty((Mr,), dtype=torch.float32, device=dev) for _ in range(n)]
-    t_r = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], Mr, Kr, 16, qs[i % n], ss[i % n]), 60)
+    t_r = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], Mr, Kr, 16, qs[i % n], ss[i % n]), 200, warm=50)
     res = {"workload": "vision block linears, group 16, M=4096 patches (qkv, proj, fc1, fc2)",
            "us_per_block": round(t_b * 1e6, 1), "tops": round(ops / t_b / 1e12, 1),
            "rotate_quant_g16": {"M": Mr, "K": Kr, "us": round(t_r * 1e6, 2), "bytes": per,
@@ -365,7 +376,7 @@ def rq_passes(torch, cr, timer):
         xs = [torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16) for _ in range(n)]
         qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
         ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
-        t = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], m, k, GROUP, qs[i % n], ss[i % n]), 60, warm=5)
+        t = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], m, k, GROUP, qs[i % n], ss[i % n]), 200, warm=50)
         res.append({"M": m, "K": k, "us": round(t * 1e6, 2), "bytes": per,
                     "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4)})
         del xs, qs, ss
@@ -396,7 +407,7 @@ def rmsnorm_rq_pass(torch, cr, wl, timer):
     res = {"M": m, "K": k, "bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "traffic": load_traffic("rmsnorm_rotate_quant_M8704_K4096", RQ_SOURCES)}
     for name, fn in runs.items():
-        t = timer.time(fn, 60, warm=5)
+        t = timer.time(fn, 200, warm=50)
         res[name] = {"us": round(t * 1e6, 2), "bytes": per[name], "achieved": round(per[name] / t / 1e9, 1),
                      "frac": round(per[name] / t / 1e9 / PEAK_HBM_GBS, 4)}
     del xs, qs, ss, ys
@@ -425,12 +436,17 @@ def vendor_int_mm(torch, cr, wl, timer):
 
 
 def copy_peak(torch, timer):
-    """Measured device-to-device copy bandwidth (1 GiB, read + write bytes)."""
-    a = torch.empty((1 << 30,), dtype=torch.uint8, device="cuda")
+    """Measured streaming bandwidth of a 1 GiB device-to-device pass (read +
+    write bytes), for context.  Two ways: torch's copy_ (the runtime's copy
+    kernel) and an elementwise kernel that reads and writes the same bytes
+    (x + 0 on int32 words), which streams about a fifth faster here."""
+    a = torch.zeros((1 << 28,), dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
-    t = timer.time(lambda i: b.copy_(a), 10)
+    t_copy = timer.time(lambda i: b.copy_(a), 10)
+    t_ew = timer.time(lambda i: torch.add(a, 0, out=b), 10)
     del a, b
-    return round(2 * (1 << 30) / t / 1e9, 1)
+    return {"copy_": round(2 * (1 << 30) / t_copy / 1e9, 1),
+            "elementwise": round(2 * (1 << 30) / t_ew / 1e9, 1)}
 
 
 def profile_mode(mode, torch, cr, wl):
