@@ -201,18 +201,49 @@ def check_parity(torch, cr, x, w, y_dev, xq_dev, xs_dev, wq_dev, ws_dev):
 
 
 def extras_w4a8(torch, cr, wl, timer):
+    """The int4-weight linear, M=4096 K=4096 N=12288, operands cycled through
+    buffer sets larger than 2x the MALL."""
     cfg = wl.CONFIGS["C5"]
     lin = cfg.linears[0]
     x, w = wl.config_inputs("C5")
     dev = torch.device("cuda")
     wq4, ws = cr.quantize_weight(torch.from_numpy(w).to(dev), bits=4)
     xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
-    y = torch.empty((cfg.M, lin.N), dtype=torch.bfloat16, device=dev)
-    wsp = cr.workspace(cfg.M, lin.K, dev)
-    t = timer.time(lambda i: cr.w4a8_linear(xd, wq4, ws, out=y, ws=wsp), 50)
+    per = cfg.M * lin.K * 2 + lin.N * lin.K // 2 + 2 * cfg.M * lin.N
+    n = max(2, -(-2 * MALL_BYTES // per) + 1)
+    sets = [(xd.clone(), wq4.clone(), ws.clone(), torch.empty((cfg.M, lin.N), dtype=torch.bfloat16, device=dev),
+             cr.workspace(cfg.M, lin.K, dev)) for _ in range(n)]
+    t = timer.time(lambda i: cr.w4a8_linear(*sets[i % n][:3], out=sets[i % n][3], ws=sets[i % n][4]), 100)
     ops = 2.0 * cfg.M * lin.N * lin.K
+    del sets
     return {"workload": "W4A8 M=4096 K=4096 N=12288", "tops": ops / t / 1e12, "us": t * 1e6,
-            "tokens_per_s": cfg.M / t, "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS}
+            "tokens_per_s": cfg.M / t, "pct_int8_peak": ops / t / 1e12 / PEAK_INT8_TOPS, "buffer_sets": n}
+
+
+def extras_configs(torch, cr, wl, timer):
+    """The other single-linear workloads, one convrot_w8a8_linear call per
+    launch: M=16 K=512 N=256 (latency-bound; its buffers stay in the MALL),
+    M=512 K=4096 N=4096, and the MLP down shape M=2048 K=12288 N=4096 with
+    operands cycled through buffer sets larger than 2x the MALL."""
+    dev = torch.device("cuda")
+    res = {}
+    for key in ("C1", "C2", "C3d"):
+        cfg = wl.CONFIGS[key]
+        lin = cfg.linears[0]
+        x, w = wl.config_inputs(key)
+        wq, ws = cr.quantize_weight(torch.from_numpy(w).to(dev), group=GROUP, bits=8)
+        xd = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        per = cfg.M * lin.K * 2 + lin.N * lin.K + 2 * cfg.M * lin.N
+        n = min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
+        sets = [(xd.clone(), wq.clone(), ws.clone(), torch.empty((cfg.M, lin.N), dtype=torch.bfloat16, device=dev),
+                 cr.workspace(cfg.M, lin.K, dev)) for _ in range(n)]
+        t = timer.time(lambda i: cr.w8a8_linear(*sets[i % n][:3], group=GROUP, out=sets[i % n][3],
+                                                ws=sets[i % n][4]), 200)
+        ops = 2.0 * cfg.M * lin.N * lin.K
+        res[key] = {"M": cfg.M, "K": lin.K, "N": lin.N, "us": round(t * 1e6, 2), "tops": round(ops / t / 1e12, 1),
+                    "tokens_per_s": round(cfg.M / t, 1), "buffer_sets": n}
+        del sets, wq, ws, xd
+    return res
 
 
 def _ok(cr, rc):
@@ -650,6 +681,8 @@ def main():
             out["vendor_int_mm"] = vendor_int_mm(torch, cr, wl, timer)
         except RuntimeError as e:  # not every torch build exposes an int8 GEMM
             out["vendor_int_mm"] = {"error": str(e)[:200]}
+        log("extras: single linears M=16 / 512 / 2048 (K 12288)")
+        out["other_linears"] = extras_configs(torch, cr, wl, timer)
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
         log("extras: weight-only path M=2048 K=4096 N=12288")
