@@ -32,6 +32,9 @@
 // loads are interleaved one per MFMA (sched_group_barrier), the loop body has
 // no conditionals, and for K a multiple of 256 each load is one scalar M0
 // update: the stage's K offset rides in the instruction's scalar offset.
+// A 128x128 tile alone on its CU (small problems) has too short a step to
+// cover the load latency with one stage in flight; it runs four stages
+// instead, each sent three steps ahead.
 //
 // Why these choices: under sustained load this GEMM runs below the chip's top
 // clock, and the clock it holds rises when less data moves per MFMA (an
@@ -159,7 +162,7 @@ struct GemmOuts {
   int n;
 };
 
-template <int BM, int BN, bool W4>
+template <int BM, int BN, bool W4, int NS = 2>
 struct CfgK {
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int TI = WN / 32, TJ = WM / 32;
@@ -181,13 +184,20 @@ struct CfgK {
   // epilogue).  Not for 256x256: 256 accumulators per lane leave no room to
   // keep the loop-invariant load offsets live across the epilogue, and the
   // spills cost more than the overlap gains (measured).
-  static constexpr bool PERSIST = !(BM == 256 && BN == 256);
+  static constexpr bool PERSIST = NS == 2 && !(BM == 256 && BN == 256);
+  // Deeper pipelines (NS stages, NS - 1 of them in flight) take one tile
+  // per workgroup; every stage's loads go out in phase 1, at most one per
+  // MFMA over its three slices.
+  static_assert(NS == 2 || (NS <= 4 && LOADS <= 3 * NM), "stages");
+  static constexpr int Q1 = LOADS < NM ? LOADS : NM;
+  static constexpr int Q2 = LOADS - Q1 < NM ? LOADS - Q1 : NM;
+  static constexpr int Q3 = LOADS - Q1 - Q2;
 };
 
-template <int BM, int BN, bool W4, bool EVEN, bool MULTI, bool BF>
+template <int BM, int BN, bool W4, bool EVEN, bool MULTI, bool BF, int NS = 2>
 __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, const float* __restrict__ sx, int M,
                                                int K, int tiles_m, int tiles_n, const GemmOuts& outs) {
-  using C = CfgK<BM, BN, W4>;
+  using C = CfgK<BM, BN, W4, NS>;
   constexpr int WM = C::WM, WN = C::WN, TI = C::TI, TJ = C::TJ, L = C::LOADS, P2 = C::P2;
   // K counts bytes of a token row (a bf16 row of k values is 2k bytes);
   // Kb is the bytes of a weight row.
@@ -197,6 +207,12 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // keeps them interleaved.
   __shared__ __attribute__((aligned(1024))) int8_t sW0[C::W_BYTES], sW1[C::W_BYTES];
   __shared__ __attribute__((aligned(1024))) int8_t sX0[C::X_BYTES], sX1[C::X_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sW2[NS > 2 ? C::W_BYTES : 16], sX2[NS > 2 ? C::X_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) int8_t sW3[NS > 3 ? C::W_BYTES : 16], sX3[NS > 3 ? C::X_BYTES : 16];
+  // Stage buffer s (s is a constant wherever this is used: the loops over
+  // stages are unrolled).
+  auto bufw = [&](int s) -> int8_t* { return s == 0 ? sW0 : s == 1 ? sW1 : s == 2 ? sW2 : sW3; };
+  auto bufx = [&](int s) -> int8_t* { return s == 0 ? sX0 : s == 1 ? sX1 : s == 2 ? sX2 : sX3; };
   // This tile's weight-row and token scales (rows past N / M read as zero).
   __shared__ __attribute__((aligned(1024))) float sSw[256], sSx[256];
 
@@ -304,8 +320,8 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // q selects which of them: [Q0, Q1).
   auto issue = [&](int s, int k0, auto q0, auto q1) {
     constexpr int Q0 = decltype(q0)::value, Q1 = decltype(q1)::value;
-    int8_t* const sW = s ? sW1 : sW0;
-    int8_t* const sX = s ? sX1 : sX0;
+    int8_t* const sW = bufw(s);
+    int8_t* const sX = bufx(s);
     const bool live = k0 < K;  // uniform
     const __amdgpu_buffer_rsrc_t rx = live ? rsx : rsx0;
     const __amdgpu_buffer_rsrc_t rw = live ? rsw : rsw0;
@@ -360,8 +376,8 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   v4i fa[2][TI], fb[2][TJ];
   uint4 pw[TI];  // int4 weights: packed bytes of the current slice pair
   auto read = [&](int s, int sl, int b) {
-    const int8_t* bw = s ? sW1 : sW0;
-    const int8_t* bx = s ? sX1 : sX0;
+    const int8_t* bw = bufw(s);
+    const int8_t* bx = bufx(s);
     if constexpr (W4) {
       if ((sl & 1) == 0) {
 #pragma unroll
@@ -432,13 +448,20 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
     }
   };
 
-  // First tile: scales, all of stage 0, the phase-2 share of stage 1.
+  // First tile: scales, all of stage 0, the phase-2 share of stage 1 (two
+  // stages); or all of stages 0 .. NS - 2 (deeper pipelines).
   int v = blockIdx.x;
   set_tile(v);
   load_scales();
-  issue(0, 0, I0{}, IL{});
-  issue(1, 128, I0{}, IP2{});
-  wait_vmcnt<P2>();
+  if constexpr (NS == 2) {
+    issue(0, 0, I0{}, IL{});
+    issue(1, 128, I0{}, IP2{});
+    wait_vmcnt<P2>();
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue(st, st * 128, I0{}, IL{});
+    wait_vmcnt<(NS - 2) * L>();
+  }
   sync_stage();
 
   for (;;) {
@@ -450,6 +473,41 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
+    if constexpr (NS > 2) {
+      // Step kt reads stage kt from buffer kt % NS and sends stage
+      // kt + NS - 1 into the buffer step kt - 1 has freed; at its end stage
+      // kt + 1 must have landed, the NS - 2 stages after it may still be in
+      // flight.  Steps past the end of K read zeros.
+      using IQ1 = std::integral_constant<int, C::Q1>;
+      using IQ2 = std::integral_constant<int, C::Q1 + C::Q2>;
+      const int ksteps_ns = (K + 128 * NS - 1) / (128 * NS) * NS;
+      for (int kb = 0; kb < ksteps_ns; kb += NS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const int kt = kb + s;
+          const int sf = (s + NS - 1) % NS, sn = (s + 1) % NS;
+          const int kf = (kt + NS - 1) * 128;
+          read(s, 1, 1);
+          mfma(0);
+          issue(sf, kf, I0{}, IQ1{});
+          interleave_phase<NM, C::Q1, ND1>();
+          read(s, 2, 0);
+          mfma(1);
+          issue(sf, kf, IQ1{}, IQ2{});
+          interleave_phase<NM, C::Q2, ND0>();
+          read(s, 3, 1);
+          mfma(0);
+          issue(sf, kf, IQ2{}, IL{});
+          interleave_phase<NM, C::Q3, ND1>();
+          wait_vmcnt<(NS - 2) * L>();
+          sync_stage();
+          __builtin_amdgcn_sched_barrier(0);
+          read(sn, 0, 0);
+          mfma(1);
+          interleave_phase<NM, 0, ND0>();
+        }
+      }
+    } else
     for (int kb = 0; kb < ksteps; kb += 2) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -641,19 +699,19 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
 }
 
 // K a multiple of 256 (every group-256 linear): unchecked scalar-offset loads.
-template <int BM, int BN, bool W4, bool MULTI>
+template <int BM, int BN, bool W4, bool MULTI, int NS = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_kernel(const int8_t* __restrict__ X,
                                                                    const float* __restrict__ sx, int M, int K,
                                                                    int tiles_m, int tiles_n, GemmOuts outs) {
-  gemm_k128_body<BM, BN, W4, true, MULTI, false>(X, sx, M, K, tiles_m, tiles_n, outs);
+  gemm_k128_body<BM, BN, W4, true, MULTI, false, NS>(X, sx, M, K, tiles_m, tiles_n, outs);
 }
 
 // Any K (a multiple of 16, of 32 for int4 weights): every chunk range-checked.
-template <int BM, int BN, bool W4, bool MULTI>
+template <int BM, int BN, bool W4, bool MULTI, int NS = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const int8_t* __restrict__ X,
                                                                         const float* __restrict__ sx, int M, int K,
                                                                         int tiles_m, int tiles_n, GemmOuts outs) {
-  gemm_k128_body<BM, BN, W4, false, MULTI, false>(X, sx, M, K, tiles_m, tiles_n, outs);
+  gemm_k128_body<BM, BN, W4, false, MULTI, false, NS>(X, sx, M, K, tiles_m, tiles_n, outs);
 }
 
 // bf16 x bf16 -> fp32 on the same pipeline (the weight-only path's matmul):
@@ -701,7 +759,7 @@ int resident_slots(const void* kernel) {
 
 // One launch over the outputs in `d` (each a weight matrix with its
 // outputs; all share xq).  Column tiles of the outputs are concatenated.
-template <int BM, int BN, bool W4>
+template <int BM, int BN, bool W4, int NS = 2>
 hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d, int n,
                        hipStream_t stream) {
   GemmOuts outs{};
@@ -717,14 +775,16 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, con
   const int tiles_m = (M + BM - 1) / BM;
   using Kernel = void (*)(const int8_t*, const float*, int, int, int, int, GemmOuts);
   const bool even = K % 256 == 0;
-  Kernel kernel = n > 1 ? (even ? gemm_i8_k128_kernel<BM, BN, W4, true> : gemm_i8_k128_tail_kernel<BM, BN, W4, true>)
-                        : (even ? gemm_i8_k128_kernel<BM, BN, W4, false> : gemm_i8_k128_tail_kernel<BM, BN, W4, false>);
+  Kernel kernel = n > 1 ? (even ? gemm_i8_k128_kernel<BM, BN, W4, true, NS>
+                               : gemm_i8_k128_tail_kernel<BM, BN, W4, true, NS>)
+                        : (even ? gemm_i8_k128_kernel<BM, BN, W4, false, NS>
+                               : gemm_i8_k128_tail_kernel<BM, BN, W4, false, NS>);
   // Persistent configurations: as many workgroups as the device holds at
   // once (never more than there are tiles), each walking its tiles in turn;
   // otherwise one workgroup per tile.
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   int64_t slots = tiles;
-  if (CfgK<BM, BN, W4>::PERSIST) {
+  if (CfgK<BM, BN, W4, NS>::PERSIST) {
     slots = resident_slots(reinterpret_cast<const void*>(kernel));
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
   }
@@ -735,15 +795,19 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, con
 
 struct TileChoice {
   int bm, bn;
+  int ns = 2;  // pipeline stages
 };
 
-// CONVROT_GEMM_TILE=<BM>x<BN> forces one of the tile shapes above (a tuning
-// override for sweeps; every tile gives bit-identical results).
+// CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>] forces one of the tile shapes above
+// (stages 3 or 4 for 128x128 int8 only; a tuning override for sweeps: every
+// choice gives bit-identical results).
 TileChoice tile_override() {
   static const TileChoice forced = [] {
     TileChoice t{0, 0};
     if (const char* s = getenv("CONVROT_GEMM_TILE")) {
-      if (sscanf(s, "%dx%d", &t.bm, &t.bn) != 2) t = {0, 0};
+      const int got = sscanf(s, "%dx%dx%d", &t.bm, &t.bn, &t.ns);
+      if (got < 2) t = {0, 0};
+      if (got == 2) t.ns = 2;
     }
     return t;
   }();
@@ -787,6 +851,12 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   for (int o = 0; o < n; ++o) n256 = n256 && d[o].N % 256 == 0;
   if (n256 && tiles(256, 256) >= 3 * cus) return {256, 256};
   if (ksteps >= 16 && 4 * tiles(256, 192) >= 3 * cus) return {256, 192};
+  // At most one 128x128 tile per CU: nothing else on the CU hides the load
+  // latency, so the tile runs a four-stage pipeline with three stages in
+  // flight (int8 weights; M 512, K 4096, N 4096: 31.4 -> 21.7 us).  With
+  // more tiles two workgroups share each CU and the two-stage kernel is
+  // faster (M 2048, K 12288, N 4096: 131 against 135-139 us).
+  if (tiles(128, 128) <= cus) return {128, 128, 4};
   return {128, 128};
 }
 
@@ -815,6 +885,10 @@ hipError_t launch_tile(TileChoice tc, const int8_t* xq, const float* x_scale, in
   if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, W4>(xq, x_scale, M, K, d, n, stream);
+  if constexpr (!W4) {
+    if (tc.ns == 4) return launch_k128<128, 128, false, 4>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 3) return launch_k128<128, 128, false, 3>(xq, x_scale, M, K, d, n, stream);
+  }
   return launch_k128<128, 128, W4>(xq, x_scale, M, K, d, n, stream);
 }
 
