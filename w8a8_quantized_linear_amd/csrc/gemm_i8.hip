@@ -429,7 +429,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   constexpr int NQ = WN / 8;
   constexpr int P = (NQ == 12) ? 208 : WN * 2;
   constexpr int STG = (32 * P + 1023) / 1024 * 1024;
-  constexpr bool DEDICATED = BM == 256 && 2 * (C::W_BYTES + C::X_BYTES) + 2048 + 4 * STG <= 160 * 1024;
+  constexpr bool DEDICATED = NS == 2 && BM == 256 && 2 * (C::W_BYTES + C::X_BYTES) + 2048 + 4 * STG <= 160 * 1024;
   __shared__ __attribute__((aligned(1024))) int8_t sStg[DEDICATED ? 4 * STG : 16];
   static_assert(DEDICATED || 2 * STG <= C::X_BYTES, "two staging blocks must fit the stage-1 token array");
   static_assert(DEDICATED || 2 * STG <= C::W_BYTES, "two staging blocks must fit the stage-1 weight array");
@@ -840,7 +840,7 @@ struct Plan {
 // single 256x192 launch (the second launch waits for the first).  With
 // several outputs the tiles of all of them count, and 256x256 needs every
 // output's N to be a multiple of 256.
-TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
+TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, bool deep) {
   const int cus = 256;
   auto tiles = [&](int bm, int bn) {
     int64_t t = 0;
@@ -851,12 +851,16 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   for (int o = 0; o < n; ++o) n256 = n256 && d[o].N % 256 == 0;
   if (n256 && tiles(256, 256) >= 3 * cus) return {256, 256};
   if (ksteps >= 16 && 4 * tiles(256, 192) >= 3 * cus) return {256, 192};
-  // At most one 128x128 tile per CU: nothing else on the CU hides the load
-  // latency, so the tile runs a four-stage pipeline with three stages in
-  // flight (int8 weights; M 512, K 4096, N 4096: 31.4 -> 21.7 us).  With
-  // more tiles two workgroups share each CU and the two-stage kernel is
-  // faster (M 2048, K 12288, N 4096: 131 against 135-139 us).
-  if (tiles(128, 128) <= cus) return {128, 128, 4};
+  // Deeper pipelines (int8 weights only) for tiles that sit alone on their
+  // CU, where nothing else hides the load latency: 256x128 with three
+  // stages when its tiles fill between three quarters of the CUs and all of
+  // them (M 2048, K 12288, N 4096: 256 tiles, 120.5 -> 99.8 us against
+  // two-stage 128x128), else 128x128 with four stages while its tiles
+  // number at most one per CU (M 512, K 4096, N 4096: 31.4 -> 21.7 us).
+  // With more tiles two two-stage 128x128 workgroups share each CU and are
+  // as fast or faster.
+  if (deep && ksteps >= 16 && 4 * tiles(256, 128) >= 3 * cus && tiles(256, 128) <= cus) return {256, 128, 3};
+  if (deep && tiles(128, 128) <= cus) return {128, 128, 4};
   return {128, 128};
 }
 
@@ -881,14 +885,16 @@ bool plan_override(Plan& out) {
 template <bool W4>
 hipError_t launch_tile(TileChoice tc, const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d,
                        int n, hipStream_t stream) {
+  if constexpr (!W4) {  // deeper pipelines: int8 weights only
+    if (tc.ns == 3 && tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128, false, 3>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 3 && tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, false, 3>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 4 && tc.bm == 128 && tc.bn == 128) return launch_k128<128, 128, false, 4>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 3 && tc.bm == 128 && tc.bn == 128) return launch_k128<128, 128, false, 3>(xq, x_scale, M, K, d, n, stream);
+  }
   if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, W4>(xq, x_scale, M, K, d, n, stream);
-  if constexpr (!W4) {
-    if (tc.ns == 4) return launch_k128<128, 128, false, 4>(xq, x_scale, M, K, d, n, stream);
-    if (tc.ns == 3) return launch_k128<128, 128, false, 3>(xq, x_scale, M, K, d, n, stream);
-  }
   return launch_k128<128, 128, W4>(xq, x_scale, M, K, d, n, stream);
 }
 
@@ -913,7 +919,7 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     return hipSuccess;
   }
   const TileChoice forced = tile_override();
-  const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n, !W4);
   return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
 
@@ -945,7 +951,7 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t stream) {
   const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
   const TileChoice forced = tile_override();
-  const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1, false);
   if (tc.bm == 256 && tc.bn == 256) return launch_bf16<256, 256>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_bf16<256, 192>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128>(x, w, int(M), int(N), int(K), y, stream);
