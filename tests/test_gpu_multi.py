@@ -31,7 +31,7 @@ def _weights(rng, Ns, K, wbits):
 
 
 @pytest.mark.parametrize("wbits,M,K,Ns", [
-    (8, 33, 512, (512, 128, 128)),            # q/k/v-like, small M: 128x128 tiles, four stages
+    (8, 33, 512, (512, 128, 128)),            # q/k/v-like, small M: 64x128 tiles, four stages
     (8, 130, 272, (70, 257, 33)),             # ragged N and K (tail kernel)
     (8, 300, 1024, (16,) * 8),                # eight tiny outputs
     (8, 2048, 512, (4096, 1024, 1024)),       # 256x192 tiles across three outputs

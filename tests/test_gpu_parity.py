@@ -43,7 +43,8 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
     (8, 2048, 4096, 768),    # 128x128
     (8, 2048, 4096, 2048),   # 256x128 with three stages, one tile per CU
     (8, 1990, 4090, 2064),   # the same, ragged M, N and K
-    (8, 512, 4000, 1040),    # 128x128 with four stages, ragged N and K
+    (8, 512, 4000, 1040),    # 64x128 with four stages, ragged N and K
+    (8, 1000, 4000, 1040),   # 128x128 with four stages, ragged M, N and K
     (8, 2000, 12280, 512),   # 256x192, ragged M and N (N not a multiple of 8)
     (8, 8700, 12288, 256),   # 256x256, ragged M
     (4, 2048, 12288, 512),   # packed int4, 256x192

@@ -32,7 +32,7 @@
 // loads are interleaved one per MFMA (sched_group_barrier), the loop body has
 // no conditionals, and for K a multiple of 256 each load is one scalar M0
 // update: the stage's K offset rides in the instruction's scalar offset.
-// A 128x128 tile alone on its CU (small problems) has too short a step to
+// A small tile alone on its CU (small problems) has too short a step to
 // cover the load latency with one stage in flight; it runs four stages
 // instead, each sent three steps ahead.
 //
@@ -177,7 +177,7 @@ struct CfgK {
   // last one still has two slices of MFMAs before the wait.
   static constexpr int P2 = (LOADS + 1) / 2;
   static constexpr int G0 = LOADS - P2;
-  static_assert(P2 <= NM && G0 <= NM, "at most one load per MFMA");
+  static_assert(NS > 2 || (P2 <= NM && G0 <= NM), "at most one load per MFMA");
   static_assert(W_LOADS * 4096 == W_BYTES && X_LOADS * 4096 == X_BYTES, "tile must split into 4 KB");
   static_assert(LOADS < 64, "vmcnt budget");
   // Persistent tile walk (the next tile's first loads overlap this tile's
@@ -799,8 +799,9 @@ struct TileChoice {
 };
 
 // CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>] forces one of the tile shapes above
-// (stages 3 or 4 for 128x128 int8 only; a tuning override for sweeps: every
-// choice gives bit-identical results).
+// (the deeper pipelines for int8 weights only: 256x128x3, 128x256x3,
+// 128x128x3, 128x128x4, 64x128x4, 128x64x4; a tuning override for sweeps:
+// every choice gives bit-identical results).
 TileChoice tile_override() {
   static const TileChoice forced = [] {
     TileChoice t{0, 0};
@@ -855,11 +856,13 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, b
   // CU, where nothing else hides the load latency: 256x128 with three
   // stages when its tiles fill between three quarters of the CUs and all of
   // them (M 2048, K 12288, N 4096: 256 tiles, 120.5 -> 99.8 us against
-  // two-stage 128x128), else 128x128 with four stages while its tiles
-  // number at most one per CU (M 512, K 4096, N 4096: 31.4 -> 21.7 us).
-  // With more tiles two two-stage 128x128 workgroups share each CU and are
-  // as fast or faster.
+  // two-stage 128x128); for small problems the smallest tile that still
+  // leaves at most one per CU, with four stages (M 512, K 4096, N 4096:
+  // 64x128, 31.4 -> 17.0 us; M 1024, K 4096, N 4096: 128x128, 23.2 us
+  // against 32.9 for 64x128 in two rounds).  With more tiles two two-stage
+  // 128x128 workgroups share each CU and are as fast or faster.
   if (deep && ksteps >= 16 && 4 * tiles(256, 128) >= 3 * cus && tiles(256, 128) <= cus) return {256, 128, 3};
+  if (deep && tiles(64, 128) <= cus) return {64, 128, 4};
   if (deep && tiles(128, 128) <= cus) return {128, 128, 4};
   return {128, 128};
 }
@@ -890,6 +893,8 @@ hipError_t launch_tile(TileChoice tc, const int8_t* xq, const float* x_scale, in
     if (tc.ns == 3 && tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, false, 3>(xq, x_scale, M, K, d, n, stream);
     if (tc.ns == 4 && tc.bm == 128 && tc.bn == 128) return launch_k128<128, 128, false, 4>(xq, x_scale, M, K, d, n, stream);
     if (tc.ns == 3 && tc.bm == 128 && tc.bn == 128) return launch_k128<128, 128, false, 3>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 4 && tc.bm == 64 && tc.bn == 128) return launch_k128<64, 128, false, 4>(xq, x_scale, M, K, d, n, stream);
+    if (tc.ns == 4 && tc.bm == 128 && tc.bn == 64) return launch_k128<128, 64, false, 4>(xq, x_scale, M, K, d, n, stream);
   }
   if (tc.bm == 256 && tc.bn == 256) return launch_k128<256, 256, W4>(xq, x_scale, M, K, d, n, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_k128<256, 192, W4>(xq, x_scale, M, K, d, n, stream);
