@@ -830,7 +830,7 @@ struct Plan {
 // Tile plan, from measurements on MI355X under sustained load.  The chip
 // runs this GEMM below its top clock, and the clock rises when less data
 // moves per MFMA, so the largest tile (256x256: fewest L2->LDS bytes per
-// operation) wins once it fills several whole rounds of the 256 CUs;
+// operation) wins once it fills several whole rounds of the CUs;
 // otherwise 256x192 when it fills at least three quarters of a round, and
 // 128x128 for small problems (more CUs busy).  With a short K (fewer than 16
 // stages of 128 bytes per token row) a tile's set-up and epilogue weigh as
@@ -841,8 +841,27 @@ struct Plan {
 // single 256x192 launch (the second launch waits for the first).  With
 // several outputs the tiles of all of them count, and 256x256 needs every
 // output's N to be a multiple of 256.
+// Compute units of the current device (256 on MI355X; fewer on a
+// partitioned device), memoised per device; 256 if the query fails.
+int device_cus() {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static int cache[kDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache[dev] > 0) return cache[dev];
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  cache[dev] = cus;
+  return cus;
+}
+
 TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, bool deep) {
-  const int cus = 256;
+  const int cus = device_cus();
   auto tiles = [&](int bm, int bn) {
     int64_t t = 0;
     for (int o = 0; o < n; ++o) t += (d[o].N + bn - 1) / bn;
