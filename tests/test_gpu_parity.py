@@ -49,6 +49,9 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
     (8, 8700, 12288, 256),   # 256x256, ragged M
     (4, 2048, 12288, 512),   # packed int4, 256x192
     (4, 4000, 12288, 256),   # packed int4, 256x256, ragged M
+    (4, 1990, 4090, 2080),   # packed int4, 256x128 with three stages, ragged M, N and K
+    (4, 1000, 4000, 1056),   # packed int4, 128x128 with four stages
+    (4, 512, 4000, 1056),    # packed int4, 64x128 with four stages
 ])
 def test_gemm_i8_large_sampled(lib, wbits, M, N, K):
     """Shapes whose tile plan uses the large tiles (persistent or not),
