@@ -718,10 +718,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_i8_k128_tail_kernel(const in
 // a stage still moves 128 bytes of every row, i.e. 64 K values, and each
 // MFMA (v_mfma_f32_32x32x16_bf16) takes the same 16 bytes per lane per
 // operand as the int8 one.  K here counts row BYTES.
-template <int BM, int BN, bool EVEN>
+template <int BM, int BN, bool EVEN, int NS = 2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t* __restrict__ X, int M, int K,
                                                                     int tiles_m, int tiles_n, GemmOuts outs) {
-  gemm_k128_body<BM, BN, false, EVEN, false, true>(X, nullptr, M, K, tiles_m, tiles_n, outs);
+  gemm_k128_body<BM, BN, false, EVEN, false, true, NS>(X, nullptr, M, K, tiles_m, tiles_n, outs);
 }
 
 // Workgroups of `kernel` the current device runs at once: compute units x
@@ -799,9 +799,10 @@ struct TileChoice {
 };
 
 // CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>] forces one of the tile shapes above
-// (the deeper pipelines, int8 and int4 weights: 256x128x3, 128x256x3,
-// 128x128x3, 128x128x4, 64x128x4, 128x64x4; a tuning override for sweeps:
-// every choice gives bit-identical results).
+// (the deeper pipelines: 256x128x3, 128x256x3, 128x128x3, 128x128x4,
+// 64x128x4, 128x64x4 for int8 and int4 weights, the first, fourth and fifth
+// for bf16; a tuning override for sweeps: every choice gives bit-identical
+// results).
 TileChoice tile_override() {
   static const TileChoice forced = [] {
     TileChoice t{0, 0};
@@ -860,7 +861,7 @@ int device_cus() {
   return cus;
 }
 
-TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, bool deep) {
+TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   const int cus = device_cus();
   auto tiles = [&](int bm, int bn) {
     int64_t t = 0;
@@ -871,9 +872,10 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, b
   for (int o = 0; o < n; ++o) n256 = n256 && d[o].N % 256 == 0;
   if (n256 && tiles(256, 256) >= 3 * cus) return {256, 256};
   if (ksteps >= 16 && 4 * tiles(256, 192) >= 3 * cus) return {256, 192};
-  // Deeper pipelines (int8 and int4 weights; not the bf16 matmul) for tiles
-  // that sit alone on their CU, where nothing else hides the load latency
-  // (int4, M 512, K 4096, N 4096: 26.9 -> 15.4 us): 256x128 with three
+  // Deeper pipelines (int8, int4 and bf16 operands) for tiles that sit
+  // alone on their CU, where nothing else hides the load latency (int4,
+  // M 512, K 4096, N 4096: 26.9 -> 15.4 us; bf16, same shape: 54.1 ->
+  // 26.5 us): 256x128 with three
   // stages when its tiles fill between three quarters of the CUs and all of
   // them (M 2048, K 12288, N 4096: 256 tiles, 120.5 -> 99.8 us against
   // two-stage 128x128); for small problems the smallest tile that still
@@ -881,9 +883,9 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n, b
   // 64x128, 31.4 -> 17.0 us; M 1024, K 4096, N 4096: 128x128, 23.2 us
   // against 32.9 for 64x128 in two rounds).  With more tiles two two-stage
   // 128x128 workgroups share each CU and are as fast or faster.
-  if (deep && ksteps >= 16 && 4 * tiles(256, 128) >= 3 * cus && tiles(256, 128) <= cus) return {256, 128, 3};
-  if (deep && tiles(64, 128) <= cus) return {64, 128, 4};
-  if (deep && tiles(128, 128) <= cus) return {128, 128, 4};
+  if (ksteps >= 16 && 4 * tiles(256, 128) >= 3 * cus && tiles(256, 128) <= cus) return {256, 128, 3};
+  if (tiles(64, 128) <= cus) return {64, 128, 4};
+  if (tiles(128, 128) <= cus) return {128, 128, 4};
   return {128, 128};
 }
 
@@ -943,11 +945,11 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     return hipSuccess;
   }
   const TileChoice forced = tile_override();
-  const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n, true);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
   return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int NS = 2>
 hipError_t launch_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K, uint16_t* y, hipStream_t stream) {
   GemmOuts outs{};
   outs.n = 1;
@@ -956,10 +958,11 @@ hipError_t launch_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K
   const int kbytes = 2 * K;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   using Kernel = void (*)(const int8_t*, int, int, int, int, GemmOuts);
-  const Kernel kernel = kbytes % 256 == 0 ? gemm_bf16_k64_kernel<BM, BN, true> : gemm_bf16_k64_kernel<BM, BN, false>;
+  const Kernel kernel =
+      kbytes % 256 == 0 ? gemm_bf16_k64_kernel<BM, BN, true, NS> : gemm_bf16_k64_kernel<BM, BN, false, NS>;
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   int64_t slots = tiles;
-  if (CfgK<BM, BN, false>::PERSIST) {
+  if (CfgK<BM, BN, false, NS>::PERSIST) {
     slots = resident_slots(reinterpret_cast<const void*>(kernel));
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
   }
@@ -975,7 +978,10 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t stream) {
   const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
   const TileChoice forced = tile_override();
-  const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1, false);
+  const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1);
+  if (tc.ns == 3 && tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128, 3>(x, w, int(M), int(N), int(K), y, stream);
+  if (tc.ns == 4 && tc.bm == 128 && tc.bn == 128) return launch_bf16<128, 128, 4>(x, w, int(M), int(N), int(K), y, stream);
+  if (tc.ns == 4 && tc.bm == 64 && tc.bn == 128) return launch_bf16<64, 128, 4>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 256) return launch_bf16<256, 256>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_bf16<256, 192>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128>(x, w, int(M), int(N), int(K), y, stream);
