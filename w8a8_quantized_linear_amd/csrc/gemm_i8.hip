@@ -32,15 +32,16 @@
 // loads are interleaved one per MFMA (sched_group_barrier), the loop body has
 // no conditionals, and for K a multiple of 256 each load is one scalar M0
 // update: the stage's K offset rides in the instruction's scalar offset.
-// A small tile alone on its CU (small problems) has too short a step to
-// cover the load latency with one stage in flight; it runs four stages
-// instead, each sent three steps ahead.
+// A tile alone on its CU (few tiles) has nothing else on the CU to hide the
+// load latency, and a small tile's step is too short to cover it with one
+// stage in flight: such tiles run three stages (256x128) or four (128x128,
+// 64x128), each sent two or three steps ahead (template parameter NS).
 //
 // Why these choices: under sustained load this GEMM runs below the chip's top
 // clock, and the clock it holds rises when less data moves per MFMA (an
 // MFMA-only loop holds ~2.27 GHz; removing the global->LDS loads from this
 // kernel gives +25 % throughput at the same power, removing the LDS reads
-// +6 %).  So the largest tile that fills the machine wins (see choose_plan),
+// +6 %).  So the largest tile that fills the machine wins (see choose_tile),
 // and per-load instruction overhead matters as much as bandwidth.
 //
 // LDS layouts, chosen by measuring ds_read_b128 throughput for these exact
