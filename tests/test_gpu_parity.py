@@ -226,6 +226,25 @@ def test_quantize_weight_i4_parity(lib, N, K, g):
     assert np.abs(q).max() <= 7
 
 
+@pytest.mark.parametrize("g", [1, 256])
+def test_quantize_weight_i4_zero_rows_keep_the_larger_c(lib, g):
+    """All-zero rows (every clip candidate has error 0) take the first
+    candidate, c = 1.00, as the oracle does; a normal row beside them is
+    unaffected."""
+    say(f"quantize_weight i4 zero rows group={g}")
+    K = 512
+    w = np.zeros((3, K), dtype=np.float32)
+    w[1] = wl.make_weight(1, K, seed=77)[0]
+    wq4, ws, ci = lib.quantize_weight(to_dev(w), group=g, bits=4, with_clip_index=True)
+    wq4_ref, ws_ref, ci_ref = oracle.quantize_weight_i4(w, g)
+    ci = ci.cpu().numpy()
+    assert ci_ref[0] == 0 and ci_ref[2] == 0
+    assert np.array_equal(ci, ci_ref)
+    assert np.array_equal(ws.cpu().numpy(), ws_ref) or np.allclose(ws.cpu().numpy(), ws_ref, rtol=4 * 2.0 ** -23)
+    q = oracle.unpack_i4(wq4.cpu().numpy())
+    assert not q[0].any() and not q[2].any()
+
+
 # -------------------------------------------------------------- end to end
 
 def _linear_full(lib, key):

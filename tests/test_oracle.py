@@ -436,6 +436,27 @@ def test_int4_clip_search_brute_force(oracle_mod, N, seed, heavy):
         assert np.abs(q[n]).max() <= 7
 
 
+def test_int4_clip_ties_keep_the_larger_c(oracle_mod):
+    """Equal errors keep the first candidate, i.e. the larger clip factor
+    (the tie rule read for the clip search of 'MossInt4', 'Format').  Two
+    closed-form ties (group 1, so the row is not rotated):
+      - an all-zero row: every candidate has scale 0, codes 0 and error 0;
+      - one subnormal value v = 513 * 2^-149: c = 1.00 and c = 0.99 both give
+        the fp32 scale 73 * 2^-149 (513/7 = 73.3 and 513 * 0.99/7 = 72.6 round
+        to 73 units), code 7 and error (7 * 73 - 513)^2 units^2, the minimum
+        (c = 0.98 gives 72 units and a larger error)."""
+    K = 32
+    w = np.zeros((2, K), dtype=np.float32)
+    w[1, 0] = np.float32(513 * 2.0 ** -149)
+    assert w[1, 0] == 513 * 2.0 ** -149
+    wq4, s, ci = oracle_mod.quantize_weight_i4(w, 1)
+    q = oracle_mod.unpack_i4(wq4)
+    assert ci[0] == 0 and s[0] == 0 and not q[0].any()
+    assert ci[1] == 0
+    assert s[1] == np.float32(73 * 2.0 ** -149)
+    assert q[1, 0] == 7 and not q[1, 1:].any()
+
+
 def test_int4_error_analogue(oracle_mod):
     """Mean relative row error on rotated Gaussian rows is in the range of the
     page's 11.4 % on real weights ('MossInt4', 'Format'); a consistency check,

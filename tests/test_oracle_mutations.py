@@ -38,6 +38,7 @@ MUTANTS = [
     ("int4_divisor_8", "(double)(100 - i) / 700.0", "(double)(100 - i) / 800.0"),
     ("no_sign_extension", "(int8_t)(lo >= 8 ? lo - 16 : lo);", "(int8_t)(lo);"),
     ("int4_no_search", "for (int i = 0; i <= 50; ++i) {", "for (int i = 0; i <= 0; ++i) {"),
+    ("int4_ties_to_smaller_c", "if (i == 0 || e < best_err) {", "if (i == 0 || e <= best_err) {"),
     ("rmsnorm_w_not_one_plus_w", "const float u = t * (1.0f + w[k]);", "const float u = t * w[k];"),
     ("rmsnorm_sum_not_mean", "const float ms = (float)(ss / (double)K);", "const float ms = (float)ss;"),
     ("rmsnorm_no_root", "const float r = 1.0f / sqrtf(ms + eps);", "const float r = 1.0f / (ms + eps);"),
@@ -68,7 +69,7 @@ PIN_TESTS = [
     "test_epilogue_order_and_bf16_ties", "test_epilogue_multiplies_token_scale_first",
     "test_rotation_suppresses_outlier_error",
     "test_unpack_all_256_bytes", "test_worked_nibble_order", "test_worked_int4_equal_magnitude",
-    "test_int4_clip_search_brute_force",
+    "test_int4_clip_search_brute_force", "test_int4_clip_ties_keep_the_larger_c",
     "test_rmsnorm_constant_power_of_two_rows", "test_rmsnorm_one_hot_gives_sqrt_k",
     "test_rmsnorm_weight_enters_as_one_plus_w", "test_rmsnorm_eps_inside_the_root",
     "test_rmsnorm_zero_row_and_unit_rms",
