@@ -39,6 +39,10 @@ MUTANTS = [
     ("no_sign_extension", "(int8_t)(lo >= 8 ? lo - 16 : lo);", "(int8_t)(lo);"),
     ("int4_no_search", "for (int i = 0; i <= 50; ++i) {", "for (int i = 0; i <= 0; ++i) {"),
     ("int4_ties_to_smaller_c", "if (i == 0 || e < best_err) {", "if (i == 0 || e <= best_err) {"),
+    ("amax_first_group_only", "    for (int64_t k = 0; k < K; ++k) {\n        float a = fabsf(v[k]);",
+     "    for (int64_t k = 0; k < (K < 256 ? K : 256); ++k) {\n        float a = fabsf(v[k]);"),
+    ("int4_amax_unrotated", "if (fabsf(rot32[k]) > amax) amax = fabsf(rot32[k]);",
+     "if (fabsf((float)in[k]) > amax) amax = fabsf((float)in[k]);"),
     ("rmsnorm_w_not_one_plus_w", "const float u = t * (1.0f + w[k]);", "const float u = t * w[k];"),
     ("rmsnorm_sum_not_mean", "const float ms = (float)(ss / (double)K);", "const float ms = (float)ss;"),
     ("rmsnorm_no_root", "const float r = 1.0f / sqrtf(ms + eps);", "const float r = 1.0f / (ms + eps);"),
