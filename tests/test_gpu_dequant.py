@@ -39,6 +39,7 @@ def assert_gemm_bf16_close(y_gpu, y_ref, x_bits, w_bits, rows=None, what="y"):
 @pytest.mark.parametrize("wbits,N,K,g", [
     (8, 64, 512, 256), (8, 300, 4096, 256), (8, 33, 1152, 16), (8, 40, 2048, 64), (8, 17, 4096, 4), (8, 9, 1024, 1),
     (4, 64, 512, 256), (4, 100, 4096, 256), (4, 20, 1152, 16), (8, 5, 32768, 256),
+    (8, 7, 768, 256), (4, 3, 256, 256), (8, 12288, 4096, 256),   # partial last workgroup; full size
 ])
 def test_dequantize_bit_exact(lib, wbits, N, K, g):
     say(f"dequantize W{wbits} N={N} K={K} group={g}")

@@ -51,6 +51,11 @@ hipError_t launch_quantize_weight_i4(const void* w, int in_dtype, int64_t rows, 
 hipError_t launch_dequantize_weight(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
                                     int log2g, uint16_t* out, hipStream_t stream);
 
+// Fast path of the above for group 256 (K a multiple of 256); returns
+// hipErrorNotSupported without launching otherwise.
+hipError_t launch_dequantize_g256(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
+                                  uint16_t* out, hipStream_t stream);
+
 // y = bf16(x . w^T) for bf16 x [M, K] and w [N, K], fp32 accumulation
 // (the matmul of the weight-only path).
 hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* y,

@@ -432,6 +432,10 @@ hipError_t dispatch_dequant(const void* wq, const float* w_scale, int64_t rows, 
 
 hipError_t launch_dequantize_weight(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
                                     int log2g, uint16_t* out, hipStream_t stream) {
+  if (log2g == 8) {
+    const hipError_t e = launch_dequantize_g256(wq, wbits, w_scale, rows, K, out, stream);
+    if (e != hipErrorNotSupported) return e;
+  }
   if (wbits == 4) return dispatch_dequant<true>(wq, w_scale, rows, K, log2g, out, stream);
   return dispatch_dequant<false>(wq, w_scale, rows, K, log2g, out, stream);
 }

@@ -32,6 +32,7 @@
 // (tests/host/quotient_identities.c).
 #include "convrot_internal.h"
 
+#include <cstdint>
 #include <cstdlib>
 
 namespace convrot {
@@ -558,6 +559,71 @@ hipError_t launch_small_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, f
 #undef CONVROT_SMALL
 }
 
+// ---------------------------------------------------------------------------
+// Weight-only path, group 256: undo the rotation of stored codes.  A group
+// of 256 codes is one DPP row of 16 lanes, lane i holding chunk u(i) as in
+// the rotate-quant kernel, so the same butterflies give the transform t of
+// the codes (integers below 2^15 in magnitude, exact in fp32 in any order)
+// with the lane's known sign; the value s_w * (t * 2^-4) is rounded to bf16.
+// t * 2^-4 is formed as fma(v, sign * 2^-4, +0), exact, which also turns a
+// zero t into +0 as the plain transform gives it (a bare sign flip would
+// leave -0 there).  Groups never straddle rows (K is a
+// multiple of 256), so the matrix is walked as a flat list of groups.
+// ("MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file table
+// row "Matmul": the weight can be dequantized for a bf16 matmul.)
+template <bool W4>
+__global__ __launch_bounds__(kThreads) void dequant_g256_kernel(const void* __restrict__ wq,
+                                                                const float* __restrict__ w_scale, int64_t ngroups,
+                                                                int groups_per_row, uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane & 15;
+  const int u = g ^ ((g & 4) ? 3 : 0);
+  const float c0 = (u & 1) ? -1.f : 1.f;
+  const float c1 = (u & 2) ? -1.f : 1.f;
+  const float c2 = (u & 4) ? -1.f : 1.f;
+  const float c3 = (u & 8) ? -1.f : 1.f;
+  const float sgn = c0 * c1 * c2 * c3;
+  // One group per 16 lanes; uniform over a DPP row, so a row that is past
+  // the end leaves together and the others' row-local DPP is unaffected.
+  const int64_t grp = (int64_t(blockIdx.x) * kThreads + threadIdx.x) >> 4;
+  if (grp >= ngroups) return;
+  float v[16];
+  if constexpr (W4) {
+    const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(wq) + grp * 128 + u * 8);
+    const uint32_t w[2] = {b.x, b.y};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // low nibble first; the bit-0 butterfly on each pair
+      const uint32_t byte = w[i / 4] >> (8 * (i % 4));
+      const float lo = float(int((byte & 0xfu) ^ 8u) - 8), hi = float(int(((byte >> 4) & 0xfu) ^ 8u) - 8);
+      v[2 * i] = lo + hi;
+      v[2 * i + 1] = lo - hi;
+    }
+  } else {
+    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(wq) + grp * 256 + u * 16);
+    const uint32_t w[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float lo = float(int8_t(w[i / 2] >> (16 * (i % 2)))), hi = float(int8_t(w[i / 2] >> (16 * (i % 2) + 8)));
+      v[2 * i] = lo + hi;
+      v[2 * i + 1] = lo - hi;
+    }
+  }
+  fwht16_rest(v);
+  stage_xor1(v, c0);
+  stage_xor2(v, c1);
+  stage_xor7(v, c2);
+  stage_xor8(v, c3);
+  const float s = w_scale[grp / groups_per_row];
+  const float sg = sgn * 0.0625f;
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    o[i] = pack_bf16x2(s * __builtin_fmaf(v[2 * i], sg, 0.0f), s * __builtin_fmaf(v[2 * i + 1], sg, 0.0f));
+  u32x4* dst = reinterpret_cast<u32x4*>(out + grp * 256 + u * 16);
+  dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+  dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 }  // namespace
 
 // Group 16 or 1 (log2g 4 or 0), bf16 activations, K <= 8192; otherwise
@@ -574,6 +640,23 @@ hipError_t launch_rotate_quant_small(const uint16_t* x, int64_t M, int64_t K, in
 hipError_t launch_rotate_quant_g256(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs,
                                     hipStream_t stream) {
   return launch_k<false>(x, M, K, xq, xs, nullptr, 0.f, nullptr, stream);
+}
+
+// Group 256 (any K that is a multiple of 256); hipErrorNotSupported
+// without launching otherwise.
+hipError_t launch_dequantize_g256(const void* wq, int wbits, const float* w_scale, int64_t rows, int64_t K,
+                                  uint16_t* out, hipStream_t stream) {
+  if (K % 256 != 0 || K / 256 > INT32_MAX) return hipErrorNotSupported;
+  const int64_t ngroups = rows * (K / 256);
+  const int64_t blocks = (ngroups * 16 + kThreads - 1) / kThreads;
+  if (blocks > INT32_MAX) return hipErrorNotSupported;
+  if (wbits == 4)
+    hipLaunchKernelGGL(dequant_g256_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, wq, w_scale,
+                       ngroups, int(K / 256), out);
+  else
+    hipLaunchKernelGGL(dequant_g256_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, wq, w_scale,
+                       ngroups, int(K / 256), out);
+  return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm_rotate_quant_g256(const uint16_t* x, const float* norm_w, float eps, int64_t M,
