@@ -70,7 +70,8 @@ def test_dequantize_odd_groups_within_one_step(lib, g):
     assert np.count_nonzero(d) <= 1e-3 * d.size
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (33, 70, 208), (130, 257, 272), (64, 512, 4096), (7, 1024, 12288)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (33, 70, 208), (130, 257, 272), (64, 512, 4096), (7, 1024, 12288),
+                                   (64, 512, 1088)])
 def test_gemm_bf16_full(lib, M, N, K):
     say(f"gemm_bf16 M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N + K)
@@ -81,7 +82,7 @@ def test_gemm_bf16_full(lib, M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2048, 12288, 512), (8704, 4096, 256), (2000, 12280, 528), (4096, 12288, 256),
-                                   (2048, 4096, 6144), (1990, 4090, 2064), (1000, 4000, 1040)])
+                                   (2048, 4096, 6144), (1990, 4090, 2064), (1000, 4000, 1040), (2048, 4096, 1088)])
 def test_gemm_bf16_large_sampled(lib, M, N, K):
     """The large tile plans (persistent 256x192, 256x256, ragged edges) and
     the deeper pipelines (256x128 three-stage, even and ragged; 128x128

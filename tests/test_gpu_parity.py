@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 GEMM_SHAPES = [
     (1, 1, 16), (16, 256, 512), (33, 70, 208), (128, 128, 128), (130, 257, 272),
     (300, 200, 1040), (512, 4096, 4096), (7, 1024, 12288),
+    (300, 200, 1152), (77, 130, 384),     # K a multiple of 128 but not 256 (unchecked loads, odd step count)
 ]
 
 
@@ -41,6 +42,7 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
     (8, 2048, 12288, 512),   # 256x192, persistent
     (8, 8704, 4096, 256),    # 256x192, three tiles per workgroup
     (8, 2048, 4096, 768),    # 128x128
+    (8, 2048, 4096, 640),    # 128x128, K an odd number of 128-steps
     (8, 2048, 4096, 2048),   # 256x128 with three stages, one tile per CU
     (8, 1990, 4090, 2064),   # the same, ragged M, N and K
     (8, 512, 4000, 1040),    # 64x128 with four stages, ragged N and K
@@ -79,7 +81,8 @@ def test_gemm_i8_large_sampled(lib, wbits, M, N, K):
     assert np.array_equal(bf16_from_dev(y[rows.tolist()]), yref)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 256, 512), (33, 70, 224), (130, 257, 4096), (64, 12288, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (16, 256, 512), (33, 70, 224), (130, 257, 4096), (64, 12288, 4096),
+                                   (130, 257, 1152)])
 def test_gemm_w4_bit_exact(lib, M, N, K):
     say(f"gemm_i8 W4 M={M} N={N} K={K}")
     rng = np.random.default_rng(2000 + M + N + K)
