@@ -608,6 +608,20 @@ def main():
     ops = 2.0 * M * N * K
     tops = ops / t_step / 1e12
 
+    # Five more timed runs of the same steps (after the headline region, so
+    # they do not affect it): the spread of the per-step time.
+    reps = []
+    for r in range(5):
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for i in range(args.steps):
+            step(i)
+        s1.record()
+        s1.synchronize()
+        reps.append(s0.elapsed_time(s1) / args.steps)
+    reps.sort()
+
     # Per-kernel durations, live, on the launch stream.
     q = [cr.rotate_quant(s[0]) for s in sets]
     t_gemm = timer.time(lambda i: cr.convrot_gemm_i8(q[i % nsets][0], q[i % nsets][1], sets[i % nsets][1], 8,
@@ -646,6 +660,8 @@ def main():
         "tokens_per_s": round(M / t_step, 1),
         "pct_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
         "hot_tops": round(ops / t_hot / 1e12, 2),
+        "step_repeats": {"runs": len(reps), "steps_each": args.steps, "median_ms": round(reps[len(reps) // 2], 5),
+                         "min_ms": round(reps[0], 5), "max_ms": round(reps[-1], 5)},
         "roofline": {
             "bound": "mfma",
             "kernel": "gemm_i8_k128_kernel (int8 MFMA GEMM + bf16 epilogue)",
