@@ -128,3 +128,28 @@ def test_dequant_path_is_closer_to_full_precision(lib):
     e_8 = np.linalg.norm(y_8 - ref) / np.linalg.norm(ref)
     say(f"rel L2 vs full precision: dequant {e_dq:.3e}, w8a8 {e_8:.3e}")
     assert e_dq <= e_8
+
+
+@pytest.mark.parametrize("M,N,K", [(4100, 12288, 528), (3000, 7000, 1504), (2000, 4000, 3008), (300, 3000, 2000),
+                                   (1000, 4000, 1008), (3000, 3000, 608)])
+def test_gemm_bf16_irregular_guarded(lib, M, N, K):
+    """Irregular shapes on every tile plan of the bf16 matmul (256x256,
+    256x192, 256x128 three-stage, 64x128 and 128x128 four-stage, 128x128):
+    sampled rows within the accumulation bound of the oracle, and guard
+    words around the output untouched."""
+    import torch
+    say(f"gemm_bf16 irregular M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 2 * N + 3 * K)
+    x = wl.float_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    w = wl.float_to_bf16_bits((rng.standard_normal((N, K)) * 0.02).astype(np.float32))
+    guard = 64
+    buf = torch.full((guard + M * N + guard,), 0x1234, dtype=torch.int16, device="cuda")
+    y = buf[guard:guard + M * N]
+    rc = lib.convrot_gemm_bf16(bf16_to_dev(x), bf16_to_dev(w), M, N, K, y)
+    torch.cuda.synchronize()
+    assert rc == 0
+    h = buf.cpu().numpy()
+    assert np.all(h[:guard] == 0x1234) and np.all(h[guard + M * N:] == 0x1234)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), [0, M - 1]]))
+    got = h[guard:guard + M * N].reshape(M, N)[rows].view(np.uint16)
+    assert_gemm_bf16_close(got, oracle.gemm_bf16(x[rows], w), x[rows], w)
