@@ -148,9 +148,21 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
   auto slot_ok = [&](int j) { return ((j * TW + wt) * 4 + (lane >> 4)) < nvalid; };
 
   u32x4 raw[C][2];
+  // Every slot in use (the common widths: 16, 32, 48 and 64 groups): plain
+  // loads, with no zero fill to keep for the masked case.
+  const bool full = nvalid == 4 * C * TW;  // uniform
   auto load = [&](int64_t tok) {
     if (tok < M) {
       const uint16_t* row = x + tok * K;
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < C; ++j) {
+          const u32x4* p = reinterpret_cast<const u32x4*>(row + chunk_off(j));
+          raw[j][0] = __builtin_nontemporal_load(p);
+          raw[j][1] = __builtin_nontemporal_load(p + 1);
+        }
+        return;
+      }
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         if (slot_ok(j)) {
