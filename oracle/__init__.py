@@ -66,6 +66,7 @@ def _load():
         "oracle_epilogue": (I, [P, P, P, I64, I64, P]),
         "oracle_w8a8_linear": (I, [P, I64, I64, P, P, I64, I, P]),
         "oracle_quantize_weight_i4": (I, [P, I64, I64, I, P, P, P]),
+        "oracle_quantize_weight_i4_ex": (I, [P, I64, I64, I, P, P, P, P, P]),
         "oracle_unpack_i4": (I, [P, I64, I64, P]),
         "oracle_w4a8_linear": (I, [P, I64, I64, P, P, I64, I, P]),
         "oracle_rmsnorm_bf16": (I, [P, P, ctypes.c_float, I64, I64, P]),
@@ -73,6 +74,7 @@ def _load():
         "oracle_dequantize_weight": (I, [P, P, I64, I64, I, P]),
         "oracle_gemm_bf16": (I, [P, P, I64, I64, I64, P]),
         "oracle_num_threads": (I, []),
+        "oracle_set_num_threads": (None, [I]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -100,6 +102,11 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's row loops use from now on."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def hadamard(g: int) -> np.ndarray:
@@ -175,16 +182,25 @@ def w8a8_linear(x_bf16: np.ndarray, wq: np.ndarray, w_scale: np.ndarray, group: 
     return y
 
 
-def quantize_weight_i4(w: np.ndarray, group: int = 256):
-    """W fp32 [N, K] -> (wq4 uint8 [N, K/2], w_scale fp32 [N], clip index int32 [N])."""
+def quantize_weight_i4(w: np.ndarray, group: int = 256, force_index=None, with_errors: bool = False):
+    """W fp32 [N, K] -> (wq4 uint8 [N, K/2], w_scale fp32 [N], clip index int32 [N]
+    [, errors fp64 [N, 51]]).
+
+    force_index (int [N], values 0..50) makes row n take that clip candidate
+    instead of the argmin; with_errors also returns every candidate's error."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     N, K = w.shape
     wq4 = np.empty((N, K // 2), dtype=np.uint8)
     s = np.empty((N,), dtype=np.float32)
     ci = np.empty((N,), dtype=np.int32)
-    _check(_load().oracle_quantize_weight_i4(_ptr(w), N, K, int(group), _ptr(wq4), _ptr(s), _ptr(ci)),
+    fi = None if force_index is None else np.ascontiguousarray(force_index, dtype=np.int32)
+    if fi is not None:
+        assert fi.shape == (N,)
+    err = np.empty((N, 51), dtype=np.float64) if with_errors else None
+    _check(_load().oracle_quantize_weight_i4_ex(_ptr(w), N, K, int(group), None if fi is None else _ptr(fi),
+                                                _ptr(wq4), _ptr(s), _ptr(ci), None if err is None else _ptr(err)),
            "quantize_weight_i4")
-    return wq4, s, ci
+    return (wq4, s, ci, err) if with_errors else (wq4, s, ci)
 
 
 def unpack_i4(wq4: np.ndarray) -> np.ndarray:

@@ -24,23 +24,28 @@
  *  - Hadamard: Sylvester construction in natural order,
  *    H[i][j] = (-1)^popcount(i & j) / sqrt(g); rotation is x' = x * H applied
  *    to each contiguous group of g columns along K.  g = 1 means no rotation.
- *  - Decision precision: the rotation is computed here in fp64 by an explicit
- *    dense matrix product (not a fast transform); the rotated value is then
- *    rounded to fp32 and every step that decides an integer code (absmax,
- *    scale, quotient, rounding) is taken in fp32, the precision of the kernel.
- *  - scale = absmax / 127 (fp32, correctly rounded); code =
- *    round_half_away_from_zero(value / scale) clamped to [-127, 127]; an
- *    all-zero row gets scale 0 and codes 0.
+ *  - Precision: the rotation is computed here in fp64 by an explicit dense
+ *    matrix product (not a fast transform) and is never rounded to a narrower
+ *    type.  The absmax is taken over those fp64 values; the scale alone is
+ *    rounded to fp32 (the pages store one fp32 scale per row); each code is
+ *    decided on the fp64 quotient value / (double)scale.  This is the plain
+ *    definition; a kernel that rotates and divides in fp32 can land on the
+ *    other side of a rounding boundary, by one code, on rare elements.
+ *  - scale = (float)(absmax / 127); code = round_half_away_from_zero(value /
+ *    scale) clamped to [-127, 127]; an all-zero row gets scale 0 and codes 0.
  *  - GEMM: naive triple loop, exact integer accumulation.
  *  - Epilogue: y = bf16_rne(((float)acc * s_x[m]) * s_w[n]) in fp32.
  *  - int4: codes in [-7, 7]; clip factor c from 1.00 down to 0.50 in steps of
- *    0.01; scale = c * absmax / 7; the c with the smallest sum of squared
- *    reconstruction error wins (ties to the larger c); byte j of a row holds
- *    column 2j in its low nibble and column 2j+1 in its high nibble.
+ *    0.01; scale = (float)(c * absmax / 7) with the fp64 absmax; codes decided
+ *    on the fp64 quotient as for int8; the c with the smallest sum of squared
+ *    reconstruction error (fp64, against the fp64 rotated row) wins (ties to
+ *    the larger c); byte j of a row holds column 2j in its low nibble and
+ *    column 2j+1 in its high nibble.
  *  - Weight-only (dequant) path ([P1] row "Matmul", [P2]): W^ = (wq * s_w)
- *    * H, computed as the exact +-1 transform of the codes times s_w times
- *    1/sqrt(g) in fp64, rounded to fp32 and then to bf16; then a bf16 matmul
- *    whose sum is taken in fp64 and rounded to fp32 and then to bf16.
+ *    * H, with the integer +-1 transform of the codes taken exactly and the
+ *    1/sqrt(g) applied once (so only that irrational constant rounds), a zero
+ *    result +0, rounded to fp32 and then to bf16; then a bf16 matmul whose
+ *    sum is taken in fp64 and rounded to fp32 and then to bf16.
  *  - RMSNorm before the linear ([P1] rows "Changed" and "How it was made":
  *    SmoothQuant scales folded into the norm weight as (1 + w) / s - 1): the
  *    norm multiplies by (1 + w); mean square over the whole row, eps inside
@@ -88,8 +93,8 @@ static uint16_t float_to_bf16_rne(float f) {
     return (uint16_t)kept;
 }
 
-/* Round half away from zero (C's roundf is exactly this). */
-static float round_half_away(float v) { return roundf(v); }
+/* Round half away from zero (C's round is exactly this). */
+static double round_half_away(double v) { return round(v); }
 
 static int is_pow2(int64_t g) { return g > 0 && (g & (g - 1)) == 0; }
 
@@ -105,7 +110,8 @@ void oracle_hadamard(int g, double *H) {
 
 /* Rotate one row of K values in fp64: for every group of g contiguous
  * columns, out[j] = sum_i in[i] * H[i][j] (dense product, [P1] "Quantized"
- * and "Matmul" rows: the same Hadamard rotates weight rows and inputs). */
+ * and "Matmul" rows: one rotation serves the weight rows and the
+ * activations). */
 static void rotate_row_f64(const double *in, int64_t K, int g, const double *H, double *out) {
     for (int64_t base = 0; base < K; base += g) {
         for (int j = 0; j < g; ++j) {
@@ -132,27 +138,24 @@ int oracle_rotate_rows(const double *x, int64_t rows, int64_t K, int g, double *
 
 /* ------------------------------------------------- int8 row quantization */
 
-/* Quantize one rotated row (already rounded to fp32) with a symmetric int8
- * grid: scale = absmax/127, code = round_half_away(v / scale).
- * ([P1] "Quantized": int8 with one fp32 scale per output row; "Matmul": the
- * input is rounded to int8 per token; [P2] "Quantization Recipe":
- * --scaling_mode row --simple, i.e. plain rounding.) */
-static void quantize_row_i8(const float *v, int64_t K, int8_t *q, float *scale) {
-    float amax = 0.0f;
+/* Quantize one rotated row (fp64 values) with a symmetric int8 grid:
+ * scale = (float)(absmax/127), code = round_half_away(v / scale) on the fp64
+ * quotient.  ([P1] "Quantized": int8 with one fp32 scale per output row;
+ * "Matmul": activations get one int8 scale per token; [P2] "Quantization
+ * Recipe": --scaling_mode row --simple, i.e. plain rounding.) */
+static void quantize_row_i8(const double *v, int64_t K, int8_t *q, float *scale) {
+    double amax = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        float a = fabsf(v[k]);
+        double a = fabs(v[k]);
         if (a > amax) amax = a;
     }
-    /* fp32 / fp32 done in fp64 then rounded once more to fp32 equals the
-     * correctly rounded fp32 quotient (53 >= 2*24 + 2). */
-    float s = (float)((double)amax / 127.0);
+    float s = (float)(amax / 127.0);
     *scale = s;
     for (int64_t k = 0; k < K; ++k) {
         if (s == 0.0f) { q[k] = 0; continue; }
-        float t = (float)((double)v[k] / (double)s);
-        float r = round_half_away(t);
-        if (r > 127.0f) r = 127.0f;
-        if (r < -127.0f) r = -127.0f;
+        double r = round_half_away(v[k] / (double)s);
+        if (r > 127.0) r = 127.0;
+        if (r < -127.0) r = -127.0;
         q[k] = (int8_t)r;
     }
 }
@@ -167,15 +170,13 @@ int oracle_quantize_weight_i8(const float *w, int64_t N, int64_t K, int g, int8_
     {
         double *in = (double *)malloc(sizeof(double) * (size_t)K);
         double *rot = (double *)malloc(sizeof(double) * (size_t)K);
-        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             for (int64_t k = 0; k < K; ++k) in[k] = (double)w[n * K + k];
             rotate_row_f64(in, K, g, H, rot);
-            for (int64_t k = 0; k < K; ++k) rot32[k] = (float)rot[k];
-            quantize_row_i8(rot32, K, wq + n * K, scale + n);
+            quantize_row_i8(rot, K, wq + n * K, scale + n);
         }
-        free(in); free(rot); free(rot32);
+        free(in); free(rot);
     }
     free(H);
     return ORACLE_OK;
@@ -192,15 +193,13 @@ int oracle_rotate_quant(const uint16_t *x, int64_t M, int64_t K, int g, int8_t *
     {
         double *in = (double *)malloc(sizeof(double) * (size_t)K);
         double *rot = (double *)malloc(sizeof(double) * (size_t)K);
-        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
 #pragma omp for schedule(static)
         for (int64_t m = 0; m < M; ++m) {
             for (int64_t k = 0; k < K; ++k) in[k] = bf16_bits_to_double(x[m * K + k]);
             rotate_row_f64(in, K, g, H, rot);
-            for (int64_t k = 0; k < K; ++k) rot32[k] = (float)rot[k];
-            quantize_row_i8(rot32, K, xq + m * K, x_scale + m);
+            quantize_row_i8(rot, K, xq + m * K, x_scale + m);
         }
-        free(in); free(rot); free(rot32);
+        free(in); free(rot);
     }
     free(H);
     return ORACLE_OK;
@@ -266,39 +265,45 @@ int oracle_w8a8_linear(const uint16_t *x, int64_t M, int64_t K, const int8_t *wq
  * s = c * absmax / 7, evaluated as absmax * (100 - i) / 700 in fp64 and
  * rounded to fp32 ([P5] "Format": one F32 scale per row chosen by a clip
  * search per row). */
-static float int4_candidate_scale(float amax, int i) {
-    return (float)((double)amax * (double)(100 - i) / 700.0);
+static float int4_candidate_scale(double amax, int i) {
+    return (float)(amax * (double)(100 - i) / 700.0);
 }
 
-/* Codes of a row for a given scale: round_half_away(v / s) clamped to
- * [-7, 7] (signed 4-bit codes, [P5] "Format"). */
-static void int4_codes(const float *v, int64_t K, float s, int8_t *q) {
+/* Codes of a row for a given scale: round_half_away(v / s) on the fp64
+ * quotient, clamped to [-7, 7] (signed 4-bit codes, [P5] "Format"). */
+static void int4_codes(const double *v, int64_t K, float s, int8_t *q) {
     for (int64_t k = 0; k < K; ++k) {
         if (s == 0.0f) { q[k] = 0; continue; }
-        float t = (float)((double)v[k] / (double)s);
-        float r = round_half_away(t);
-        if (r > 7.0f) r = 7.0f;
-        if (r < -7.0f) r = -7.0f;
+        double r = round_half_away(v[k] / (double)s);
+        if (r > 7.0) r = 7.0;
+        if (r < -7.0) r = -7.0;
         q[k] = (int8_t)r;
     }
 }
 
 /* Sum of squared reconstruction error of a row, in fp64. */
-static double int4_row_error(const float *v, int64_t K, float s, const int8_t *q) {
+static double int4_row_error(const double *v, int64_t K, float s, const int8_t *q) {
     double e = 0.0;
     for (int64_t k = 0; k < K; ++k) {
-        double d = (double)q[k] * (double)s - (double)v[k];
+        double d = (double)q[k] * (double)s - v[k];
         e += d * d;
     }
     return e;
 }
 
 /* Weight preparation, int4: W fp32 [N,K] -> wq4 uint8 [N,K/2] (two signed
- * nibbles per byte, low nibble = even column), scale fp32 [N]; clip_index[n]
- * (may be NULL) receives the winning candidate i (c = 1 - i/100). */
-int oracle_quantize_weight_i4(const float *w, int64_t N, int64_t K, int g, uint8_t *wq4, float *scale,
-                              int32_t *clip_index) {
+ * nibbles per byte, low nibble = even column), scale fp32 [N].
+ *   clip_index (may be NULL) receives the winning candidate i (c = 1 - i/100);
+ *   errors (may be NULL, [N, 51]) receives every candidate's error;
+ *   force_index (may be NULL, [N]) skips the choice: row n takes candidate
+ *   force_index[n] (in 0..50) instead of the argmin.  The tests use the last
+ *   two to judge a kernel whose choice differs on a near tie. */
+int oracle_quantize_weight_i4_ex(const float *w, int64_t N, int64_t K, int g, const int32_t *force_index,
+                                 uint8_t *wq4, float *scale, int32_t *clip_index, double *errors) {
     if (!w || !wq4 || !scale || N < 0 || K <= 0 || (K & 1) || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
+    if (force_index)
+        for (int64_t n = 0; n < N; ++n)
+            if (force_index[n] < 0 || force_index[n] > 50) return ORACLE_ERR_ARG;
     double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
     if (!H) return ORACLE_ERR_ARG;
     oracle_hadamard(g, H);
@@ -306,26 +311,25 @@ int oracle_quantize_weight_i4(const float *w, int64_t N, int64_t K, int g, uint8
     {
         double *in = (double *)malloc(sizeof(double) * (size_t)K);
         double *rot = (double *)malloc(sizeof(double) * (size_t)K);
-        float *rot32 = (float *)malloc(sizeof(float) * (size_t)K);
         int8_t *q = (int8_t *)malloc((size_t)K);
         int8_t *best_q = (int8_t *)malloc((size_t)K);
 #pragma omp for schedule(static)
         for (int64_t n = 0; n < N; ++n) {
             for (int64_t k = 0; k < K; ++k) in[k] = (double)w[n * K + k];
             rotate_row_f64(in, K, g, H, rot);
-            float amax = 0.0f;
-            for (int64_t k = 0; k < K; ++k) {
-                rot32[k] = (float)rot[k];
-                if (fabsf(rot32[k]) > amax) amax = fabsf(rot32[k]);
-            }
+            double amax = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                if (fabs(rot[k]) > amax) amax = fabs(rot[k]);
             int best_i = 0;
             double best_err = 0.0;
             float best_s = 0.0f;
             for (int i = 0; i <= 50; ++i) {
                 float s = int4_candidate_scale(amax, i);
-                int4_codes(rot32, K, s, q);
-                double e = int4_row_error(rot32, K, s, q);
-                if (i == 0 || e < best_err) {
+                int4_codes(rot, K, s, q);
+                double e = int4_row_error(rot, K, s, q);
+                if (errors) errors[n * 51 + i] = e;
+                const int take = force_index ? (i == force_index[n]) : (i == 0 || e < best_err);
+                if (take) {
                     best_err = e; best_i = i; best_s = s;
                     memcpy(best_q, q, (size_t)K);
                 }
@@ -338,10 +342,16 @@ int oracle_quantize_weight_i4(const float *w, int64_t N, int64_t K, int g, uint8
                 wq4[n * (K / 2) + j] = (uint8_t)(lo | (hi << 4));
             }
         }
-        free(in); free(rot); free(rot32); free(q); free(best_q);
+        free(in); free(rot); free(q); free(best_q);
     }
     free(H);
     return ORACLE_OK;
+}
+
+/* The clip search as defined: every row takes its argmin candidate. */
+int oracle_quantize_weight_i4(const float *w, int64_t N, int64_t K, int g, uint8_t *wq4, float *scale,
+                              int32_t *clip_index) {
+    return oracle_quantize_weight_i4_ex(w, N, K, g, NULL, wq4, scale, clip_index, NULL);
 }
 
 /* Packed int4 [N,K/2] -> int8 codes [N,K]: each nibble read as a signed
@@ -417,22 +427,26 @@ int oracle_rmsnorm_rotate_quant(const uint16_t *x, const float *w, float eps, in
 
 /* ------------------------------------------------ weight-only dequant path */
 
-/* The weight-only runtime mode ([P1] file table, row "Matmul": the weight can
- * instead be dequantized for a bf16 matmul; [P2] loads the checkpoints
- * through that dequant path).  A stored row holds the codes of the ROTATED
- * weight row, so the weight is recovered by undoing the rotation:
- * W^ = (wq * s_w) * H^-1, and H^-1 = H (the normalised Sylvester matrix is
- * symmetric and orthogonal).  Written with the scalar factors of that
- * product taken out, so that it is exact wherever it can be:
- *   t_k      = sum_j code_j * sign(H[j][k])     (the +-1 pattern; an exact
- *                                                integer, |t| <= 256 * 128)
- *   u_k      = (t_k * s_w[n]) * H[0][0]         (fp64; H[0][0] = 1/sqrt(g),
- *                                                a power of two, so exact,
- *                                                for even log2(g))
- *   W^[n][k] = bf16_rne((float)u_k)             (rounded to fp32, the scale's
- *                                                precision, then to bf16)
- * per group of g columns.  int4 rows are unpacked to their codes first
- * (oracle_unpack_i4). */
+/* The weight-only runtime mode ([P1] file table, row "Matmul": a mode that
+ * expands the codes back into a bf16 weight and multiplies in bf16; [P2]
+ * loads the checkpoints through that dequant path).  A stored row holds the
+ * codes of the ROTATED weight row, so the weight is recovered by undoing the
+ * rotation: W^ = (wq * s_w) * H^-1, and H^-1 = H (the normalised Sylvester
+ * matrix is symmetric and orthogonal).  H is the +-1 Sylvester pattern times
+ * 1/sqrt(g), so per group of g columns the product is evaluated as
+ *   t_k      = sum_j code_j * sign(H[j][k])   (an integer, |t| <= 256 * 128:
+ *                                              exact in fp64, in any order)
+ *   u_k      = (t_k * s_w[n]) * H[0][0] + 0   (t * s_w exact in fp64; one
+ *                                              rounding by 1/sqrt(g), none for
+ *                                              even log2(g); + 0 makes a zero
+ *                                              result +0, as the sum of the
+ *                                              dense product's terms is)
+ *   W^[n][k] = bf16_rne((float)u_k)           (rounded to fp32, the scale's
+ *                                              precision, then to bf16)
+ * This is the product itself, exact but for the one irrational constant: an
+ * fp64 dense product would round every term by 1/sqrt(g) for odd log2(g) and
+ * leave a residue of order 1e-19 where the exact value is 0.
+ * int4 rows are unpacked to their codes first (oracle_unpack_i4). */
 int oracle_dequantize_weight(const int8_t *wq, const float *w_scale, int64_t N, int64_t K, int g, uint16_t *w_out) {
     if (!wq || !w_scale || !w_out || N < 0 || K <= 0 || !is_pow2(g) || K % g) return ORACLE_ERR_ARG;
     double *H = (double *)malloc(sizeof(double) * (size_t)g * (size_t)g);
@@ -442,12 +456,13 @@ int oracle_dequantize_weight(const int8_t *wq, const float *w_scale, int64_t N, 
 #pragma omp parallel for schedule(static)
     for (int64_t n = 0; n < N; ++n) {
         const int8_t *q = wq + n * K;
+        const double s = (double)w_scale[n];
         for (int64_t base = 0; base < K; base += g) {
             for (int k = 0; k < g; ++k) {
                 double t = 0.0;
                 for (int j = 0; j < g; ++j)
                     t += (H[(int64_t)j * g + k] > 0.0 ? 1.0 : -1.0) * (double)q[base + j];
-                const double u = (t * (double)w_scale[n]) * norm;
+                const double u = (t * s) * norm + 0.0;
                 w_out[n * K + base + k] = float_to_bf16_rne((float)u);
             }
         }
@@ -480,5 +495,16 @@ int oracle_num_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Threads for the parallel regions that follow (n >= 1); the CPU baseline
+ * times the oracle on all cores and on one. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

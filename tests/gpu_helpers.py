@@ -7,13 +7,19 @@ import numpy as np
 #  - int32 accumulators from identical int8 codes: bit-exact;
 #  - bf16 outputs from identical codes and scales: bit-exact (same formula,
 #    same fp32 operation order, RNE);
-#  - int8 codes produced by the GPU's fp32 fast Walsh-Hadamard transform vs
-#    the oracle's fp64 dense product: identical except at most 1 LSB on at
-#    most 0.01 % of the elements (the two rotations round differently, which
-#    can move a value across a rounding boundary);
+#  - int8 codes produced by the GPU's fp32 fast Walsh-Hadamard transform and
+#    fp32 quotient vs the oracle's exact fp64 rotation and fp64 quotient:
+#    identical except at most 1 LSB on at most 0.01 % of the elements (the
+#    fp32 roundings can move a value across a rounding boundary);
+#  - on small structured rows, where 0.01 % is less than one element: codes
+#    identical except where the oracle's exact quotient lies within 2^-12 of
+#    a rounding boundary n + 1/2 (there they may differ by one);
+#  - int4 clip choice: the oracle's error at the GPU's candidate within a
+#    near-tie bound of the oracle's minimum (see assert_clip_choice);
 #  - fp32 scales: within 4 ulp (absmax can differ by the same rounding);
 #  - bf16 end-to-end outputs: relative L2 <= 1e-3.
 CODE_MISMATCH_MAX_FRAC = 1e-4
+NEAR_TIE = 2.0 ** -12
 SCALE_RTOL = 4 * 2.0 ** -23
 REL_L2_MAX = 1e-3
 
@@ -52,11 +58,18 @@ def code_mismatch(q_gpu, q_ref):
     return (int(np.abs(d).max()) if d.size else 0), (np.count_nonzero(d) / max(d.size, 1))
 
 
-def assert_codes_close(q_gpu, q_ref, what="codes"):
+def assert_codes_close(q_gpu, q_ref, what="codes", q_exact=None):
+    """At most 1 LSB apart, on at most 0.01 % of the elements (counted as at
+    most max(1, 1e-4 n), so that a single rounding tie in a small test does
+    not fail it); with the oracle's exact quotients at hand, every differing
+    code must also sit at a rounding boundary (assert_codes_off_ties)."""
     assert q_gpu.shape == q_ref.shape, (q_gpu.shape, q_ref.shape)
     mx, frac = code_mismatch(q_gpu, q_ref)
     assert mx <= 1, f"{what}: max code difference {mx}"
-    assert frac <= CODE_MISMATCH_MAX_FRAC, f"{what}: {frac:.3e} of codes differ"
+    n_diff = int(round(frac * q_gpu.size))
+    assert n_diff <= max(1, CODE_MISMATCH_MAX_FRAC * q_gpu.size), f"{what}: {frac:.3e} of codes differ ({n_diff})"
+    if q_exact is not None:
+        assert_codes_off_ties(q_gpu, q_ref, q_exact, what)
     return frac
 
 
@@ -80,3 +93,56 @@ def assert_rel_l2(y_gpu_bits, y_ref_bits, what="y"):
     r = rel_l2(y_gpu_bits, y_ref_bits)
     assert r <= REL_L2_MAX, f"{what}: relative L2 {r:.3e}"
     return r
+
+
+def exact_quotients(x_f64, scales, group):
+    """The oracle's exact rotated rows (fp64 dense product) divided by the
+    stored fp32 scales, in fp64: the values the oracle's codes round."""
+    import oracle
+    rot = oracle.rotate_rows(np.asarray(x_f64, dtype=np.float64), group)
+    s = np.asarray(scales, dtype=np.float64)
+    return rot / np.where(s == 0, 1.0, s)[:, None]
+
+
+def assert_codes_off_ties(q_gpu, q_ref, q_exact, what="codes"):
+    """Codes equal the oracle's except where the exact quotient lies within
+    NEAR_TIE of a rounding boundary n + 1/2, where they may differ by one
+    (the GPU rotates and divides in fp32, which can land a value on the
+    other side of such a boundary).  Returns the number of codes that differ."""
+    assert q_gpu.shape == q_ref.shape == q_exact.shape
+    d = q_gpu.astype(np.int16) - q_ref.astype(np.int16)
+    a = np.abs(q_exact)
+    near = np.abs(a - np.floor(a) - 0.5) <= NEAR_TIE
+    assert np.abs(d).max(initial=0) <= 1, f"{what}: a code differs by more than one"
+    bad = (d != 0) & ~near
+    assert not bad.any(), f"{what}: {int(bad.sum())} codes differ away from a rounding boundary"
+    return int(np.count_nonzero(d))
+
+
+# Near-tie bound of the int4 clip choice.  Each candidate's error e(c) =
+# sum_k (q_k s - v_k)^2 is continuous in the rotated row v and the scale s.
+# The GPU evaluates it (in fp64) on its fp32 rotation and on scales taken from
+# its fp32 absmax; with those within eta * |v|_2 (eta = 2^-20, sixteen fp32
+# ulps of the row norm) the two evaluations of one candidate differ by at most
+# about 4 eta sqrt(e) |v|_2, so a choice can flip only between candidates whose
+# exact errors differ by twice that.  The bound below is 2^-16 sqrt(e) |v|_2,
+# a factor two above it.
+CLIP_TIE_FACTOR = 2.0 ** -16
+
+
+def assert_clip_choice(ci_gpu, errors, rot_norm, what="clip index", max_frac=0.01):
+    """int4 clip search: the GPU's candidate per row is the oracle's argmin,
+    or a near tie with it: errors[n, ci_gpu[n]] - min_c errors[n, c] <=
+    CLIP_TIE_FACTOR * sqrt(errors[n, ci_gpu[n]]) * |rotated row n|_2.  Rows
+    off the argmin must stay rare (at most max_frac of them)."""
+    n = np.arange(errors.shape[0])
+    e_gpu = errors[n, ci_gpu]
+    e_min = errors.min(axis=1)
+    slack = e_gpu - e_min
+    off = ci_gpu != errors.argmin(axis=1)
+    assert off.mean() <= max_frac, f"{what}: {int(off.sum())} rows off the argmin"
+    bound = CLIP_TIE_FACTOR * np.sqrt(e_gpu) * rot_norm
+    bad = slack > bound
+    assert not bad.any(), (f"{what}: rows {np.nonzero(bad)[0][:8].tolist()} are not near ties "
+                           f"(slack {slack[bad][:4]}, bound {bound[bad][:4]})")
+    return int(off.sum())

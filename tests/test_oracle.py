@@ -37,19 +37,23 @@ def ref_rotate(x64, g):
 
 
 def ref_half_away(v):
-    """Round half away from zero, written with floor on |v| (exact in fp64)."""
+    """Round half away from zero in fp64, exactly: v - trunc(v) is exact for
+    |v| < 2^52, so the comparison with 1/2 is too (floor(|v| + 0.5) would
+    misround 0.49999999999999994)."""
     v = np.asarray(v, dtype=np.float64)
-    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+    t = np.trunc(v)
+    return t + np.sign(v) * (np.abs(v - t) >= 0.5)
 
 
-def ref_quant_rows(rot32, qmax=127):
-    """Per-row symmetric quantization, independent numpy formulation."""
-    rot32 = rot32.astype(np.float32)
-    amax = np.abs(rot32).max(axis=1)
-    s = (amax / np.float32(qmax)).astype(np.float32)       # fp32 IEEE division
-    safe = np.where(s == 0, np.float32(1), s)
-    t = (rot32 / safe[:, None]).astype(np.float32)          # fp32 IEEE division
-    q = np.clip(ref_half_away(t), -qmax, qmax)
+def ref_quant_rows(rot64, qmax=127):
+    """Per-row symmetric quantization of fp64 rotated rows, independent numpy
+    formulation of the plain definition: fp64 absmax, the scale rounded once
+    to fp32, codes decided on the fp64 quotient."""
+    rot64 = np.asarray(rot64, dtype=np.float64)
+    amax = np.abs(rot64).max(axis=1)
+    s = (amax / qmax).astype(np.float32)                    # fp64 divide, one rounding to fp32
+    safe = np.where(s == 0, np.float32(1), s).astype(np.float64)
+    q = np.clip(ref_half_away(rot64 / safe[:, None]), -qmax, qmax)
     q[s == 0] = 0
     return q.astype(np.int8), s
 
@@ -163,6 +167,23 @@ def test_worked_identity_group_ties(oracle_mod):
     assert xq[0].tolist() == ex["codes"]
 
 
+def test_worked_quotient_decided_in_fp64(oracle_mod):
+    ex = golden("worked_examples.json")["quotient_decided_in_fp64"]
+    w = np.array([[int(h, 16) for h in ex["w_bits_hex"]]], dtype=np.uint32).view(np.float32)
+    wq, ws = oracle_mod.quantize_weight_i8(w, ex["group"])
+    assert ws[0].view(np.uint32) == int(ex["scale_bits_hex"], 16)
+    assert wq[0].tolist() == ex["codes"]
+
+
+def test_worked_rotation_kept_in_fp64(oracle_mod):
+    ex = golden("worked_examples.json")["rotation_kept_in_fp64"]
+    xb = bf16(np.array([ex["x"]]))
+    assert np.array_equal(wl.bf16_bits_to_float(xb)[0].astype(np.float64), np.array(ex["x"]))  # exact in bf16
+    xq, s = oracle_mod.rotate_quant(xb, ex["group"])
+    assert s[0] == ex["scale"]
+    assert xq[0].tolist() == ex["codes"]
+
+
 def test_zero_row(oracle_mod):
     xq, s = oracle_mod.rotate_quant(np.zeros((2, 512), dtype=np.uint16), 256)
     assert np.all(s == 0) and np.all(xq == 0)
@@ -190,9 +211,9 @@ def test_scale_is_absmax_over_127(oracle_mod):
     rng = np.random.default_rng(4)
     xb = _rand_bf16(rng, 32, 768, outliers=7)
     _, s = oracle_mod.rotate_quant(xb, 256)
-    rot = ref_rotate(wl.bf16_bits_to_float(xb).astype(np.float64), 256).astype(np.float32)
+    rot = ref_rotate(wl.bf16_bits_to_float(xb).astype(np.float64), 256)
     amax = np.abs(rot).max(axis=1)
-    assert np.array_equal(s, (amax / np.float32(127)).astype(np.float32))
+    assert np.array_equal(s, (amax / 127.0).astype(np.float32))
 
 
 def test_scale_invariance_power_of_two(oracle_mod):
@@ -215,8 +236,8 @@ def test_rotate_quant_brute_force_tiny(oracle_mod, M, G, seed, outliers, scale_e
         x[:, rng.choice(K, outliers, replace=False)] *= 20
     xb = bf16(x)
     xq, s = oracle_mod.rotate_quant(xb, 256)
-    rot32 = ref_rotate(wl.bf16_bits_to_float(xb).astype(np.float64), 256).astype(np.float32)
-    q_ref, s_ref = ref_quant_rows(rot32)
+    rot = ref_rotate(wl.bf16_bits_to_float(xb).astype(np.float64), 256)
+    q_ref, s_ref = ref_quant_rows(rot)
     assert np.array_equal(s, s_ref)
     assert np.array_equal(xq, q_ref)
 
@@ -228,8 +249,8 @@ def test_quantize_weight_i8_brute_force_tiny(oracle_mod, N, G, seed):
     K = 256 * G
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     wq, ws = oracle_mod.quantize_weight_i8(w, 256)
-    rot32 = ref_rotate(w.astype(np.float64), 256).astype(np.float32)
-    q_ref, s_ref = ref_quant_rows(rot32)
+    rot = ref_rotate(w.astype(np.float64), 256)
+    q_ref, s_ref = ref_quant_rows(rot)
     assert np.array_equal(ws, s_ref)
     assert np.array_equal(wq, q_ref)
     assert ws.dtype == np.float32 and ws.shape == (N,)  # one fp32 scale per output row
@@ -239,7 +260,7 @@ def test_group_one_is_plain_rowwise(oracle_mod):
     rng = np.random.default_rng(6)
     w = (rng.standard_normal((4, 64)) * 0.02).astype(np.float32)
     wq, ws = oracle_mod.quantize_weight_i8(w, 1)
-    q_ref, s_ref = ref_quant_rows(w)
+    q_ref, s_ref = ref_quant_rows(w.astype(np.float64))
     assert np.array_equal(wq, q_ref) and np.array_equal(ws, s_ref)
 
 
@@ -401,20 +422,24 @@ def test_worked_int4_equal_magnitude(oracle_mod):
     assert np.array_equal(np.sign(q), np.sign(w).astype(np.int8))
 
 
-def _ref_int4_row(rot32_row):
-    """Brute-force clip search for one rotated fp32 row, independent numpy."""
-    amax = np.float32(np.abs(rot32_row).max())
-    best = None
+def _ref_int4_row(rot_row):
+    """Brute-force clip search for one fp64 rotated row, independent numpy:
+    every candidate's scale from the fp64 absmax, codes on the fp64 quotient,
+    fp64 error; returns (best error, index, scale, codes, all errors)."""
+    rot_row = np.asarray(rot_row, dtype=np.float64)
+    amax = np.abs(rot_row).max()
+    best, errs = None, []
     for i in range(51):
-        s = np.float32(np.float64(amax) * (100 - i) / 700.0)
+        s = np.float32(amax * (100 - i) / 700.0)
         if s == 0:
-            q = np.zeros_like(rot32_row)
+            q = np.zeros_like(rot_row)
         else:
-            q = np.clip(ref_half_away((rot32_row / s).astype(np.float32)), -7, 7)
-        err = float(np.sum((q.astype(np.float64) * np.float64(s) - rot32_row.astype(np.float64)) ** 2))
+            q = np.clip(ref_half_away(rot_row / np.float64(s)), -7, 7)
+        err = float(np.sum((q * np.float64(s) - rot_row) ** 2))
+        errs.append(err)
         if best is None or err < best[0]:
             best = (err, i, s, q.astype(np.int8))
-    return best
+    return best + (np.array(errs),)
 
 
 @settings(max_examples=15, deadline=None)
@@ -425,15 +450,40 @@ def test_int4_clip_search_brute_force(oracle_mod, N, seed, heavy):
     w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
     if heavy:
         w[:, rng.choice(K, 3, replace=False)] *= 30
-    wq4, s, ci = oracle_mod.quantize_weight_i4(w, 256)
+    wq4, s, ci, errs = oracle_mod.quantize_weight_i4(w, 256, with_errors=True)
     assert wq4.shape == (N, K // 2) and wq4.dtype == np.uint8     # two codes per byte
-    rot32 = ref_rotate(w.astype(np.float64), 256).astype(np.float32)
+    rot = ref_rotate(w.astype(np.float64), 256)
     q = oracle_mod.unpack_i4(wq4)
     for n in range(N):
-        err, i, s_ref, q_ref = _ref_int4_row(rot32[n])
+        err, i, s_ref, q_ref, errs_ref = _ref_int4_row(rot[n])
         assert ci[n] == i and s[n] == s_ref
         assert np.array_equal(q[n], q_ref)
         assert np.abs(q[n]).max() <= 7
+        assert np.allclose(errs[n], errs_ref, rtol=1e-12, atol=0)
+
+
+def test_int4_forced_candidate(oracle_mod):
+    """Forcing each row's candidate gives that candidate's scale and codes
+    (checked against the numpy search), and forcing the argmin reproduces the
+    unforced result bit for bit."""
+    rng = np.random.default_rng(21)
+    N, K = 6, 512
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq4, s, ci = oracle_mod.quantize_weight_i4(w, 256)
+    wq4_f, s_f, ci_f = oracle_mod.quantize_weight_i4(w, 256, force_index=ci)
+    assert np.array_equal(wq4, wq4_f) and np.array_equal(s, s_f) and np.array_equal(ci, ci_f)
+    force = rng.integers(0, 51, N).astype(np.int32)
+    wq4_g, s_g, ci_g = oracle_mod.quantize_weight_i4(w, 256, force_index=force)
+    assert np.array_equal(ci_g, force)
+    rot = ref_rotate(w.astype(np.float64), 256)
+    q = oracle_mod.unpack_i4(wq4_g)
+    for n in range(N):
+        amax = np.abs(rot[n]).max()
+        s_ref = np.float32(amax * (100 - force[n]) / 700.0)
+        assert s_g[n] == s_ref
+        assert np.array_equal(q[n], np.clip(ref_half_away(rot[n] / np.float64(s_ref)), -7, 7).astype(np.int8))
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.quantize_weight_i4(w, 256, force_index=np.full(N, 51, np.int32))
 
 
 def test_int4_clip_ties_keep_the_larger_c(oracle_mod):
@@ -594,6 +644,31 @@ def test_dequant_one_hot_closed_form(oracle_mod, g):
         signs = scipy.linalg.hadamard(g)[j] if g > 1 else np.ones(1)
         want[b * g:(b + 1) * g] = np.float32(c * s / np.sqrt(g)) * signs
         assert np.array_equal(got, wl.bf16_bits_to_float(_bf16_of_f32(want)))
+
+
+@pytest.mark.parametrize("g", [8, 16, 32, 128, 256])
+def test_dequant_exact_zeros_are_positive_zero(oracle_mod, g):
+    """Where the exact value of (wq * s) * H is zero it dequantizes to +0.
+    Closed form: a group whose codes start (3, -1, -2) and are zero after
+    that transforms to 3 - 1 - 2 = 0 in column 0 (every entry of H's first
+    column is +1/sqrt(g)) and in some other columns (scipy's Sylvester matrix
+    says which), to nonzero values in the rest; rounding each
+    product by 1/sqrt(g) separately would leave RN(3a) - RN(a) - RN(2a), not
+    0, for odd log2(g).  A zero row scale gives +0 everywhere (never -0)."""
+    K = 2 * g
+    q = np.zeros((2, K), np.int8)
+    for b in range(K // g):
+        q[0, b * g:b * g + 3] = (3, -1, -2)
+    q[1] = np.random.default_rng(g).integers(-127, 128, K).astype(np.int8)
+    s = np.array([0.0123, 0.0], np.float32)
+    out = oracle_mod.dequantize_weight(q, s, g)
+    t = q[0, :g].astype(np.int64) @ scipy.linalg.hadamard(g)      # the integer transform of one group
+    assert t[0] == 0
+    for b in range(K // g):
+        grp = out[0, b * g:(b + 1) * g]
+        assert np.all(grp[t == 0] == 0x0000)
+        assert np.all((grp[t != 0] & 0x7fff) != 0)
+    assert np.all(out[1] == 0x0000)
 
 
 def test_dequant_group_one_is_scale_times_code(oracle_mod):
