@@ -6,8 +6,8 @@
  *  - "MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file table:
  *    row "Quantized" -- every weight row is rotated per contiguous 256-column
  *    group by a Hadamard matrix and stored int8 with one fp32 scale per output
- *    row; row "Matmul" -- at run time the input is rotated by the same
- *    Hadamard, rounded to int8 per token and multiplied in int8.
+ *    row; row "Matmul" -- at run time the activations get the group-wise
+ *    rotation too, one int8 scale per token, and the product runs in int8.
  *  - "qwen3.5_4b_int8_convrot", "Quantization Recipe": row-wise scaling with
  *    plain rounding (--scaling_mode row --simple), group size 256.
  *  - "craftingmod/Qwen3-VL-8B-Heretic-INT8", "Quantization metadata":
@@ -26,8 +26,11 @@
  *    code       = round_half_away_from_zero(rotated / scale)  (int8, |code| <= 127)
  *    acc[m][n]  = sum_k xq[m][k] * wq[n][k]                    (exact int32)
  *    y[m][n]    = bf16_rne(((float)acc[m][n] * x_scale[m]) * w_scale[n])
- * An all-zero row gets scale 0 and all codes 0.  Every decision that yields a
- * code (absmax, scale, quotient, rounding) is taken in fp32.
+ * An all-zero row gets scale 0 and all codes 0.  The definition takes the
+ * rotation and the quotient exactly, with only the scale rounded (to fp32).
+ * The kernels rotate with an fp32 fast Walsh-Hadamard transform and divide in
+ * fp32, so a code can land one step away where the exact quotient sits at a
+ * rounding boundary (a few codes in a million on Gaussian activations).
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous; bf16
@@ -40,8 +43,12 @@
  *  - Work is enqueued on `stream` (0 = the null stream) without any host
  *    synchronisation; results are valid once the stream has reached them.
  *  - Arguments are validated on the host before anything is enqueued; on a
- *    non-zero status nothing has been written.  M == 0 (or N == 0) is a
- *    successful no-op.
+ *    non-zero status nothing has been written.  M == 0 is a successful no-op
+ *    for every call that has an M.  N == 0 is a successful no-op for the
+ *    calls over weight rows alone (convrot_quantize_weight,
+ *    convrot_quantize_weight_i4_clip, convrot_dequantize_weight); the calls
+ *    that multiply (the linears and the GEMMs) return CONVROT_ERR_SHAPE for
+ *    N <= 0.
  *  - Tensor pointers must be 16-byte aligned; scale pointers 4-byte aligned.
  *  - Shapes: K % 16 == 0, K % group == 0, K <= CONVROT_MAX_K; int4 weights
  *    additionally need K % 32 == 0.  The calls that multiply (the linears
@@ -201,7 +208,8 @@ int convrot_quantize_weight_i4_clip(const void *w, int w_dtype, int64_t N, int64
 
 /*
  * Weight-only (dequant) path ("MOSS-Image ... INT8" page, file table row
- * "Matmul": the weight can instead be dequantized for a bf16 matmul;
+ * "Matmul": a weight-only mode that expands the codes back into a bf16
+ * weight and multiplies in bf16;
  * "qwen3.5_4b_int8_convrot" loads the checkpoints through that path).  The
  * activations are not quantized.
  */

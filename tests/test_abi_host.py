@@ -140,6 +140,10 @@ def test_linear_validation(L):
     assert lin8(A, 8, 512, B, C, 64, 100, D, E, need) == ERR["group"]
     assert lin4(A, 8, 528, B, C, 64, 16, D, E, need) == ERR["shape"]   # int4 needs K % 32
     assert lin8(NUL, 0, 512, NUL, NUL, 64, 256, NUL, NUL, 0) == 0
+    # N <= 0 is a shape error for every call that multiplies, even with M == 0
+    assert lin8(NUL, 0, 512, NUL, NUL, 0, 256, NUL, NUL, 0) == ERR["shape"]
+    assert lin4(NUL, 0, 512, NUL, NUL, 0, 256, NUL, NUL, 0) == ERR["shape"]
+    assert gemm(NUL, NUL, NUL, 8, NUL, 0, 0, 64, NUL, NUL) == ERR["shape"]
     assert lin8(A, 1 << 31, 512, B, C, 64, 256, D, E, need) == ERR["shape"]
 
 

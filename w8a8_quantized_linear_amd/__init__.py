@@ -117,6 +117,49 @@ def _dptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _need(t, nbytes, what):
+    """The library reads or writes nbytes of t: refuse a smaller buffer here,
+    since the C layer cannot see buffer lengths."""
+    if t is not None and _nbytes(t) < nbytes:
+        raise ValueError(f"convrot: {what} holds {_nbytes(t)} bytes, the call touches {nbytes}")
+
+
+def _expect(t, what, shape, dtypes):
+    """Shape and dtype check of one argument of an allocating helper."""
+    if t is None:
+        raise ValueError(f"convrot: {what} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"convrot: {what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"convrot: {what} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"convrot: tensors on several devices: {sorted(str(d) for d in devs)}")
+
+
+def _weight_shape(wbits, N, K):
+    torch = _torch()
+    if wbits == 8:
+        return (N, K), (torch.int8,)
+    if wbits == 4:
+        if K % 2:
+            raise ValueError("convrot: int4 weights need an even K")
+        return (N, K // 2), (torch.uint8,)
+    raise ValueError(f"convrot: wbits must be 8 or 4, got {wbits}")
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
 def _stream(stream=None):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -153,47 +196,92 @@ def convrot_workspace_size(M: int, K: int) -> int:
 
 
 def convrot_quantize_weight(w, w_dtype, N, K, group, bits, wq, w_scale, stream=None) -> int:
+    if N > 0 and K > 0:
+        _need(w, N * K * (4 if w_dtype == W_F32 else 2), "w")
+        _need(wq, N * K // (2 if bits == 4 else 1), "wq")
+        _need(w_scale, 4 * N, "w_scale")
     return load().convrot_quantize_weight(_dptr(w), int(w_dtype), int(N), int(K), int(group), int(bits),
                                           _dptr(wq), _dptr(w_scale), _stream(stream))
 
 
 def convrot_quantize_weight_i4_clip(w, w_dtype, N, K, group, wq4, w_scale, clip_index, stream=None) -> int:
+    if N > 0 and K > 0:
+        _need(w, N * K * (4 if w_dtype == W_F32 else 2), "w")
+        _need(wq4, N * K // 2, "wq4")
+        _need(w_scale, 4 * N, "w_scale")
+        _need(clip_index, 4 * N, "clip_index")
     return load().convrot_quantize_weight_i4_clip(_dptr(w), int(w_dtype), int(N), int(K), int(group),
                                                   _dptr(wq4), _dptr(w_scale), _dptr(clip_index),
                                                   _stream(stream))
 
 
 def convrot_rotate_quant(x, M, K, group, xq, x_scale, stream=None) -> int:
+    if M > 0 and K > 0:
+        _need(x, 2 * M * K, "x")
+        _need(xq, M * K, "xq")
+        _need(x_scale, 4 * M, "x_scale")
     return load().convrot_rotate_quant(_dptr(x), int(M), int(K), int(group), _dptr(xq), _dptr(x_scale),
                                        _stream(stream))
 
 
 def convrot_rmsnorm_rotate_quant(x, norm_w, eps, M, K, group, xq, x_scale, y_norm=None, stream=None) -> int:
+    if M > 0 and K > 0:
+        _need(x, 2 * M * K, "x")
+        _need(norm_w, 4 * K, "norm_w")
+        _need(xq, M * K, "xq")
+        _need(x_scale, 4 * M, "x_scale")
+        _need(y_norm, 2 * M * K, "y_norm")
     return load().convrot_rmsnorm_rotate_quant(_dptr(x), _dptr(norm_w), float(eps), int(M), int(K), int(group),
                                                _dptr(xq), _dptr(x_scale), _dptr(y_norm), _stream(stream))
 
 
+def _need_linear(x, M, K, wq, w_bytes, w_scale, N, y, workspace, workspace_bytes):
+    if M > 0 and K > 0 and N > 0:
+        _need(x, 2 * M * K, "x")
+        _need(wq, w_bytes, "wq")
+        _need(w_scale, 4 * N, "w_scale")
+        _need(y, 2 * M * N, "y")
+        _need(workspace, workspace_bytes, "workspace")
+
+
 def convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    _need_linear(x, M, K, wq, N * K, w_scale, N, y, workspace, workspace_bytes)
     return load().convrot_w8a8_linear(_dptr(x), int(M), int(K), _dptr(wq), _dptr(w_scale), int(N), int(group),
                                       _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    _need_linear(x, M, K, wq4, N * K // 2, w_scale, N, y, workspace, workspace_bytes)
     return load().convrot_w4a8_linear(_dptr(x), int(M), int(K), _dptr(wq4), _dptr(w_scale), int(N), int(group),
                                       _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc_out, y, stream=None) -> int:
+    if M > 0 and N > 0 and K > 0:
+        _need(xq, M * K, "xq")
+        _need(x_scale, 4 * M, "x_scale")
+        _need(wq, N * K // (2 if wbits == 4 else 1), "wq")
+        _need(w_scale, 4 * N, "w_scale")
+        _need(acc_out, 4 * M * N, "acc_out")
+        _need(y, 2 * M * N, "y")
     return load().convrot_gemm_i8(_dptr(xq), _dptr(x_scale), _dptr(wq), int(wbits), _dptr(w_scale), int(M),
                                   int(N), int(K), _dptr(acc_out), _dptr(y), _stream(stream))
 
 
 def convrot_dequantize_weight(wq, wbits, w_scale, N, K, group, w_out, stream=None) -> int:
+    if N > 0 and K > 0:
+        _need(wq, N * K // (2 if wbits == 4 else 1), "wq")
+        _need(w_scale, 4 * N, "w_scale")
+        _need(w_out, 2 * N * K, "w_out")
     return load().convrot_dequantize_weight(_dptr(wq), int(wbits), _dptr(w_scale), int(N), int(K), int(group),
                                             _dptr(w_out), _stream(stream))
 
 
 def convrot_gemm_bf16(x, w, M, N, K, y, stream=None) -> int:
+    if M > 0 and N > 0 and K > 0:
+        _need(x, 2 * M * K, "x")
+        _need(w, 2 * N * K, "w")
+        _need(y, 2 * M * N, "y")
     return load().convrot_gemm_bf16(_dptr(x), _dptr(w), int(M), int(N), int(K), _dptr(y), _stream(stream))
 
 
@@ -202,14 +290,22 @@ def convrot_dequant_workspace_size(N: int, K: int) -> int:
 
 
 def convrot_dequant_linear(x, M, K, wq, wbits, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:
+    _need_linear(x, M, K, wq, N * K // (2 if wbits == 4 else 1), w_scale, N, y, workspace, workspace_bytes)
     return load().convrot_dequant_linear(_dptr(x), int(M), int(K), _dptr(wq), int(wbits), _dptr(w_scale), int(N),
                                          int(group), _dptr(y), _dptr(workspace), int(workspace_bytes),
                                          _stream(stream))
 
 
-def _outs_array(outs):
+def _outs_array(outs, M=0, K=0, wbits=8):
     """Sequence of (wq, w_scale, N, acc_out, y) (tensors or None, and N) ->
-    ctypes array of LinearOut."""
+    ctypes array of LinearOut (each buffer checked against M, K and N)."""
+    if M > 0 and K > 0:
+        for wq, ws, n, acc, y in outs:
+            if n > 0:
+                _need(wq, n * K // (2 if wbits == 4 else 1), "wq")
+                _need(ws, 4 * n, "w_scale")
+                _need(acc, 4 * M * n, "acc_out")
+                _need(y, 2 * M * n, "y")
     arr = (LinearOut * max(1, len(outs)))()
     for i, (wq, ws, n, acc, y) in enumerate(outs):
         arr[i] = LinearOut(_dptr(wq), _dptr(ws), int(n), _dptr(acc), _dptr(y))
@@ -218,22 +314,65 @@ def _outs_array(outs):
 
 def convrot_gemm_i8_multi(xq, x_scale, wbits, M, K, outs, stream=None) -> int:
     """outs: sequence of (wq, w_scale, N, acc_out, y)."""
-    return load().convrot_gemm_i8_multi(_dptr(xq), _dptr(x_scale), int(wbits), int(M), int(K),
-                                        _outs_array(outs), len(outs), _stream(stream))
+    if M > 0 and K > 0:
+        _need(xq, M * K, "xq")
+        _need(x_scale, 4 * M, "x_scale")
+    arr = _outs_array(outs, M, K, wbits)
+    return load().convrot_gemm_i8_multi(_dptr(xq), _dptr(x_scale), int(wbits), int(M), int(K), arr, len(outs),
+                                        _stream(stream))
 
 
 def convrot_linear_multi(x, M, K, group, wbits, outs, workspace, workspace_bytes, stream=None) -> int:
     """outs: sequence of (wq, w_scale, N, acc_out, y)."""
-    return load().convrot_linear_multi(_dptr(x), int(M), int(K), int(group), int(wbits), _outs_array(outs),
-                                       len(outs), _dptr(workspace), int(workspace_bytes), _stream(stream))
+    if M > 0 and K > 0:
+        _need(x, 2 * M * K, "x")
+        _need(workspace, workspace_bytes, "workspace")
+    arr = _outs_array(outs, M, K, wbits)
+    return load().convrot_linear_multi(_dptr(x), int(M), int(K), int(group), int(wbits), arr, len(outs),
+                                       _dptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 # ----------------------------------------------------- allocating helpers
+# Each checks its tensors' shapes, dtypes and device before anything reaches
+# the library (ValueError on a mismatch), then allocates what it returns.
+
+def _mk(x, dtypes=None, what="x"):
+    """[M, K] of a 2-D activation-like tensor (bf16 bits by default)."""
+    if x.dim() != 2:
+        raise ValueError(f"convrot: {what} must be 2-D [M, K], got shape {tuple(x.shape)}")
+    dtypes = dtypes or _bf16_types()
+    if x.dtype not in dtypes:
+        raise ValueError(f"convrot: {what} has dtype {x.dtype}, expected one of {[str(d) for d in dtypes]}")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def _check_weight(wq, w_scale, wbits, K, what):
+    """wq is int8 [N, K] (wbits 8) or packed uint8 [N, K/2] (wbits 4), with
+    an fp32 [N] scale."""
+    torch = _torch()
+    if wq.dim() != 2:
+        raise ValueError(f"convrot: {what} must be 2-D, got shape {tuple(wq.shape)}")
+    N = int(wq.shape[0])
+    shape, dtypes = _weight_shape(wbits, N, K)
+    _expect(wq, what, shape, dtypes)
+    _expect(w_scale, f"{what} scale", (N,), (torch.float32,))
+
+
+def _check_ws(ws, nbytes):
+    torch = _torch()
+    if ws.dtype not in (torch.uint8, torch.int8) or ws.dim() != 1:
+        raise ValueError("convrot: the workspace must be a 1-D uint8 tensor")
+    if ws.numel() < nbytes:
+        raise ValueError(f"convrot: workspace of {ws.numel()} bytes, the call needs {nbytes}")
+
+
 
 def quantize_weight(w, group: int = 256, bits: int = 8, with_clip_index: bool = False):
     """w fp32/bf16 [N, K] on the GPU -> (wq, w_scale[, clip_index]).
     bits 8: wq int8 [N, K]; bits 4: wq uint8 [N, K/2] (two nibbles per byte)."""
     torch = _torch()
+    if w.dim() != 2:
+        raise ValueError(f"convrot.quantize_weight: w must be 2-D [N, K], got shape {tuple(w.shape)}")
     N, K = w.shape
     if w.dtype == torch.float32:
         wd = W_F32
@@ -241,6 +380,7 @@ def quantize_weight(w, group: int = 256, bits: int = 8, with_clip_index: bool = 
         wd = W_BF16
     else:
         raise TypeError("convrot.quantize_weight: w must be float32 or bfloat16")
+    _weight_shape(bits, N, K)
     dev = w.device
     scale = torch.empty((N,), dtype=torch.float32, device=dev)
     if bits == 8:
@@ -260,7 +400,7 @@ def rotate_quant(x, group: int = 256):
     """x bf16 [M, K] -> (xq int8 [M, K], x_scale fp32 [M])."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
+    M, K = _mk(x)
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check("convrot_rotate_quant", convrot_rotate_quant(x, M, K, group, xq, xs))
@@ -272,9 +412,9 @@ def rmsnorm_rotate_quant(x, norm_w, eps: float = 1e-6, group: int = 256, want_y:
     x bf16 [M, K], norm_w fp32 [K] -> (xq int8 [M, K], x_scale fp32 [M][, y bf16 [M, K]])."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
-    if norm_w.dtype != torch.float32:
-        raise TypeError("convrot.rmsnorm_rotate_quant: norm_w must be float32")
+    M, K = _mk(x)
+    _expect(norm_w, "norm_w", (K,), (torch.float32,))
+    _same_device(x, norm_w)
     xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     xs = torch.empty((M,), dtype=torch.float32, device=x.device)
     y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if want_y else None
@@ -289,11 +429,21 @@ def linear_multi(x, weights, wbits: int = 8, group: int = 256, outs=None, ws=Non
     outputs [M, N_o] (or fills ``outs``)."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
+    M, K = _mk(x)
+    if not 1 <= len(weights) <= MAX_OUTS:
+        raise ValueError(f"convrot.linear_multi: 1..{MAX_OUTS} weights, got {len(weights)}")
+    for i, (wq, wsc) in enumerate(weights):
+        _check_weight(wq, wsc, wbits, K, f"weights[{i}]")
     if outs is None:
         outs = [torch.empty((M, wq.shape[0]), dtype=torch.bfloat16, device=x.device) for wq, _ in weights]
+    if len(outs) != len(weights):
+        raise ValueError("convrot.linear_multi: one output per weight")
+    for i, ((wq, _), y) in enumerate(zip(weights, outs)):
+        _expect(y, f"outs[{i}]", (M, wq.shape[0]), _bf16_types())
     if ws is None:
         ws = workspace(M, K, x.device)
+    _check_ws(ws, convrot_workspace_size(M, K))
+    _same_device(x, ws, *[t for wq, wsc in weights for t in (wq, wsc)], *outs)
     desc = [(wq, wsc, wq.shape[0], None, y) for (wq, wsc), y in zip(weights, outs)]
     _check("convrot_linear_multi", convrot_linear_multi(x, M, K, group, wbits, desc, ws, ws.numel()))
     return outs
@@ -303,7 +453,13 @@ def gemm_i8_multi(xq, x_scale, weights, wbits: int = 8, want_acc: bool = True, w
     """convrot_gemm_i8 over several weight matrices sharing xq; returns a list
     of (acc int32 [M, N_o] or None, y bf16 [M, N_o] or None)."""
     torch = _torch()
-    M, K = xq.shape
+    M, K = _mk(xq, (torch.int8,), "xq")
+    _expect(x_scale, "x_scale", (M,), (torch.float32,))
+    if not 1 <= len(weights) <= MAX_OUTS:
+        raise ValueError(f"convrot.gemm_i8_multi: 1..{MAX_OUTS} weights, got {len(weights)}")
+    for i, (wq, wsc) in enumerate(weights):
+        _check_weight(wq, wsc, wbits, K, f"weights[{i}]")
+    _same_device(xq, x_scale, *[t for wq, wsc in weights for t in (wq, wsc)])
     res, desc = [], []
     for wq, wsc in weights:
         n = wq.shape[0]
@@ -319,6 +475,8 @@ def dequantize_weight(wq, w_scale, K: int, wbits: int = 8, group: int = 256):
     """Codes (int8 [N, K] or packed int4 uint8 [N, K/2]) -> bf16 weight [N, K]."""
     torch = _torch()
     N = wq.shape[0]
+    _check_weight(wq, w_scale, wbits, K, "wq")
+    _same_device(wq, w_scale)
     out = torch.empty((N, K), dtype=torch.bfloat16, device=wq.device)
     _check("convrot_dequantize_weight", convrot_dequantize_weight(wq, wbits, w_scale, N, K, group, out))
     return out
@@ -328,9 +486,12 @@ def gemm_bf16(x, w, out=None):
     """bf16 x [M, K] . w [N, K]^T -> bf16 [M, N] (fp32 accumulation)."""
     torch = _torch()
     x, w = _bits16(x), _bits16(w)
-    M, K = x.shape
+    M, K = _mk(x)
     N = w.shape[0]
+    _expect(w, "w", (N, K), _bf16_types())
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _expect(y, "out", (M, N), _bf16_types())
+    _same_device(x, w, y)
     _check("convrot_gemm_bf16", convrot_gemm_bf16(x, w, M, N, K, y))
     return y
 
@@ -339,11 +500,15 @@ def dequant_linear(x, wq, w_scale, wbits: int = 8, group: int = 256, out=None, w
     """The weight-only linear: dequantize wq (into a workspace), then the bf16 matmul."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
+    M, K = _mk(x)
     N = wq.shape[0]
+    _check_weight(wq, w_scale, wbits, K, "wq")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _expect(y, "out", (M, N), _bf16_types())
     if ws is None:
         ws = torch.empty((max(convrot_dequant_workspace_size(N, K), 16),), dtype=torch.uint8, device=x.device)
+    _check_ws(ws, convrot_dequant_workspace_size(N, K))
+    _same_device(x, wq, w_scale, y, ws)
     _check("convrot_dequant_linear",
            convrot_dequant_linear(x, M, K, wq, wbits, w_scale, N, group, y, ws, ws.numel()))
     return y
@@ -359,11 +524,15 @@ def w8a8_linear(x, wq, w_scale, group: int = 256, out=None, ws=None):
     """y = ConvRot W8A8 linear(x); x bf16 [M, K], wq int8 [N, K] -> y bf16 [M, N]."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
+    M, K = _mk(x)
     N = wq.shape[0]
+    _check_weight(wq, w_scale, 8, K, "wq")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _expect(y, "out", (M, N), _bf16_types())
     if ws is None:
         ws = workspace(M, K, x.device)
+    _check_ws(ws, convrot_workspace_size(M, K))
+    _same_device(x, wq, w_scale, y, ws)
     _check("convrot_w8a8_linear",
            convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, ws, ws.numel()))
     return y
@@ -373,11 +542,15 @@ def w4a8_linear(x, wq4, w_scale, group: int = 256, out=None, ws=None):
     """W4A8 variant; wq4 uint8 [N, K/2] -> y bf16 [M, N]."""
     torch = _torch()
     x = _bits16(x)
-    M, K = x.shape
+    M, K = _mk(x)
     N = wq4.shape[0]
+    _check_weight(wq4, w_scale, 4, K, "wq4")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _expect(y, "out", (M, N), _bf16_types())
     if ws is None:
         ws = workspace(M, K, x.device)
+    _check_ws(ws, convrot_workspace_size(M, K))
+    _same_device(x, wq4, w_scale, y, ws)
     _check("convrot_w4a8_linear",
            convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, ws, ws.numel()))
     return y
@@ -386,8 +559,16 @@ def w4a8_linear(x, wq4, w_scale, group: int = 256, out=None, ws=None):
 def gemm_i8(xq, x_scale, wq, w_scale, wbits: int = 8, want_acc: bool = True, want_y: bool = True):
     """Integer product on given codes -> (acc int32 [M, N] or None, y bf16 [M, N] or None)."""
     torch = _torch()
-    M, K = xq.shape
+    M, K = _mk(xq, (torch.int8,), "xq")
     N = wq.shape[0]
+    if want_y or x_scale is not None:
+        _expect(x_scale, "x_scale", (M,), (torch.float32,))
+    if want_y or w_scale is not None:
+        _check_weight(wq, w_scale, wbits, K, "wq")
+    else:
+        shape, dtypes = _weight_shape(wbits, N, K)
+        _expect(wq, "wq", shape, dtypes)
+    _same_device(xq, x_scale, wq, w_scale)
     acc = torch.empty((M, N), dtype=torch.int32, device=xq.device) if want_acc else None
     y = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device) if want_y else None
     _check("convrot_gemm_i8", convrot_gemm_i8(xq, x_scale, wq, wbits, w_scale, M, N, K, acc, y))
