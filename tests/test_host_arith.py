@@ -1,9 +1,10 @@
-"""Host checks of the fp32 arithmetic identities that the fast activation
-quantizer (rotate_quant_fast.hip) relies on: Markstein's corrected quotient
-equals IEEE division over the scales the kernel admits, and
-trunc(q + copysign(0.49999997, q)) rounds half away from zero.  The checker
-is a C program (tests/host/quotient_identities.c) built with gcc; two builds
-with a planted mistake must be rejected by it."""
+"""Host checks of the fp32 arithmetic the fast activation quantizer
+(rotate_quant_fast.hip) relies on: the int8 code is the low byte of
+fma(v, rb, 1.5 * 2^23) with rb = RN(1/scale) raised by two units in the
+last place, which rounds every exact tie away from zero and differs from
+round_half_away(v / scale) only just below a rounding boundary.  The
+checker is a C program (tests/host/quotient_identities.c) built with gcc;
+builds with a planted mistake must be rejected by it."""
 import pathlib
 import shutil
 import subprocess
@@ -27,13 +28,15 @@ def _run(exe):
     return subprocess.run([str(exe)], capture_output=True, text=True, timeout=300)
 
 
-def test_quotient_identities_hold(tmp_path):
+def test_quantizer_identities_hold(tmp_path):
     res = _run(_build(tmp_path, "qid"))
     assert res.returncode == 0, res.stdout + res.stderr
-    assert "markstein random: 200000000 pairs, 0 mismatches" in res.stdout
+    assert "byte identity: every |p| <= 128, 0 mismatches" in res.stdout
+    assert "not away from zero" in res.stdout and ", 0 not away from zero" in res.stdout
+    assert "decision random: 200000000 pairs, 0 off the definition away from a boundary" in res.stdout
 
 
-@pytest.mark.parametrize("plant", ["PLANT_PLAIN_HALF", "PLANT_NO_CORRECTION"])
+@pytest.mark.parametrize("plant", ["PLANT_MAGIC_2P23", "PLANT_NO_BUMP"])
 def test_checker_rejects_planted_mistake(tmp_path, plant):
     res = _run(_build(tmp_path, plant.lower(), [plant]))
     assert res.returncode != 0, res.stdout

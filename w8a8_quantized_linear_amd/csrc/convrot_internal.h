@@ -15,6 +15,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// The int8 code of a value v of a row whose scale is s (the scale's rule is
+// s = absmax / 127): code = round_half_away(v / s), taken as one fused
+// multiply-add and a byte pick.  rb = RN(1 / s) raised by two units in the
+// last place, so that |v * rb| exceeds |v / s| strictly, by at most 2^-21 of
+// it; fma(v, rb, 1.5 * 2^23) rounds v * rb to an integer once (the unit in
+// the last place there is 1, ties to even) and its low byte is that integer
+// in two's complement.  An exact tie n + 1/2 therefore rounds away from
+// zero, as the definition does, and a code differs from the definition only
+// where |v / s| lies within 2^-21 of a boundary below it (one further from
+// zero).  Valid for s in [2^-100, 2^122) or s = 0 (all codes 0); smaller
+// scales are lifted by 2^64 with their values.  The identities are checked
+// on the host (tests/host/quotient_identities.c).
+constexpr float kCodeMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kTinyScale = 0x1p-100f;    // below it, lift values and scale by 2^64
+
+__device__ __forceinline__ float code_rcp(float s) {
+  return s > 0.f ? __uint_as_float(__float_as_uint(1.0f / s) + 2u) : 0.f;
+}
+
+// The word whose low byte is the code of v (rb from code_rcp, possibly
+// carrying a sign flip shared with v).
+__device__ __forceinline__ uint32_t code_bits(float v, float rb) {
+  return __float_as_uint(__builtin_fmaf(v, rb, kCodeMagic));
+}
+
+// The low bytes of four words, in order, as one word.
+__device__ __forceinline__ uint32_t pack4_lo(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t lo = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a0 b0 0 0
+  const uint32_t hi = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);  // c0 d0 0 0
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);             // a0 b0 c0 d0
+}
+
 // x bf16 [rows, K] (in_dtype 1) or fp32 (in_dtype 0) -> codes int8 [rows, K]
 // with |code| <= qmax and fp32 scale [rows].  log2g = log2(group size).
 hipError_t launch_rotate_quant(const void* x, int in_dtype, int64_t rows, int64_t K, int log2g,

@@ -17,7 +17,9 @@
 // across waves), after which every code is decided in fp32:
 //   scale = absmax / 127,  code = round_half_away(value / scale)
 // as stated for ConvRot int8 checkpoints ("MOSS-Image Qwen3.5-9B text encoder,
-// INT8 (W8A8, ConvRot)", file table rows "Quantized" and "Matmul").
+// INT8 (W8A8, ConvRot)", file table rows "Quantized" and "Matmul"); the
+// quotient and rounding are one fma and a byte pick (code_rcp, code_bits),
+// the rule every int8 code of the library follows.
 //
 // MODE_I4 runs the int4 weight preparation of "MossInt4" ("Format"): the same
 // rotation, then a per-row clip search over c = 1.00 .. 0.50 with fp64 error
@@ -131,11 +133,6 @@ __device__ __forceinline__ double row_sum(double v, double* red) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-  return (uint32_t(a) & 0xffu) | ((uint32_t(b) & 0xffu) << 8) | ((uint32_t(c) & 0xffu) << 16) |
-         ((uint32_t(d) & 0xffu) << 24);
-}
-
 template <int TPT, int C, int IN, int MODE, bool NORM>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __restrict__ x, int64_t rows,
                                                                 int64_t K, int log2g, float inv_sqrt_g,
@@ -215,25 +212,34 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const void* __re
   if constexpr (MODE == MODE_I8) {
     // v holds rotated values times 1/pow2_norm (exact power of two), so
     // value/scale is the same quotient as v / (amax_v / 127).
-    const float s_v = amax / 127.0f;
-    if (row_ok && t == 0) scale[row] = s_v * pow2_norm;
+    float s_v = amax / 127.0f;
+    float out_mul = pow2_norm;
+    if (s_v < kTinyScale && s_v > 0.f) {
+      // Tiny row (uniform: amax is the row's): lift values and scale by 2^64
+      // so the reciprocal stays finite; for a normal s_v the quotients are
+      // exactly the unlifted ones.
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[j][i] *= 0x1p64f;
+      s_v = (amax * 0x1p64f) / 127.0f;
+      out_mul = pow2_norm * 0x1p-64f;
+    }
+    if (row_ok && t == 0) scale[row] = s_v * out_mul;
+    const float rb = code_rcp(s_v);
     int8_t* out = static_cast<int8_t*>(codes);
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const int64_t c = t + int64_t(TPT) * j;
-      int q[16];
+      uint32_t q[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float r = (s_v == 0.f) ? 0.f : roundf(v[j][i] / s_v);
-        r = fminf(fmaxf(r, -127.f), 127.f);
-        q[i] = int(r);
-      }
+      for (int i = 0; i < 16; ++i) q[i] = code_bits(v[j][i], rb);
       if (row_ok && c < nchunks) {
         uint4 o;
-        o.x = pack4_i8(q[0], q[1], q[2], q[3]);
-        o.y = pack4_i8(q[4], q[5], q[6], q[7]);
-        o.z = pack4_i8(q[8], q[9], q[10], q[11]);
-        o.w = pack4_i8(q[12], q[13], q[14], q[15]);
+        o.x = pack4_lo(q[0], q[1], q[2], q[3]);
+        o.y = pack4_lo(q[4], q[5], q[6], q[7]);
+        o.z = pack4_lo(q[8], q[9], q[10], q[11]);
+        o.w = pack4_lo(q[12], q[13], q[14], q[15]);
         *reinterpret_cast<uint4*>(out + row * K + c * 16) = o;
       }
     }
@@ -333,7 +339,7 @@ hipError_t dispatch(const void* x, int64_t rows, int64_t K, int log2g, void* cod
 // s_w * (t * 2^-(log2g/2)) with one rounding for even log2(g) (the power of
 // two is exact), or (t / sqrt(g)) * s_w for odd log2(g), and is rounded to
 // bf16.  ("MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file
-// table row "Matmul": the weight can be dequantized for a bf16 matmul.)
+// table row "Matmul": its weight-only mode expands the codes into a bf16 weight.)
 template <int TPT, int C, bool W4>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const void* __restrict__ wq,
                                                            const float* __restrict__ w_scale, int64_t rows,
@@ -379,8 +385,12 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const void* __restric
     uint32_t o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float a = odd ? (v[j][2 * i] * inv_sqrt_g) * s : s * (v[j][2 * i] * pow2_norm);
-      const float b = odd ? (v[j][2 * i + 1] * inv_sqrt_g) * s : s * (v[j][2 * i + 1] * pow2_norm);
+      // fma with +0 rounds like the product and turns a -0 (zero scale,
+      // negative transform) into the +0 that the dense product gives.
+      const float a = odd ? __builtin_fmaf(v[j][2 * i] * inv_sqrt_g, s, 0.0f)
+                          : __builtin_fmaf(s, v[j][2 * i] * pow2_norm, 0.0f);
+      const float b = odd ? __builtin_fmaf(v[j][2 * i + 1] * inv_sqrt_g, s, 0.0f)
+                          : __builtin_fmaf(s, v[j][2 * i + 1] * pow2_norm, 0.0f);
       o[i] = pack_bf16x2(a, b);
     }
     if (row_ok && c < nchunks) {

@@ -21,15 +21,16 @@
 //     a known per-lane sign (-1)^popcount(u); it is applied for free in the
 //     quantization (the sign is folded into the reciprocal and the scale).
 //
-// Quantization per element (all fp32):
-//   scale = absmax / 127;  code = round_half_away(value / scale).
-// The quotient is the correctly rounded fp32 quotient, obtained from
-// q0 = v * r (r = 1/scale, correctly rounded), e = fma(-q0, scale, v),
-// q1 = fma(e, r, q0) (Markstein's correction), valid for scales in
-// [2^-100, 2^122) (rows with a smaller scale are lifted by 2^64 first);
-// half-away-from-zero rounding is trunc(q1 + copysign(0.49999997, q1)).
-// Both identities are checked exhaustively on the host
-// (tests/host/quotient_identities.c).
+// Quantization per element: scale = absmax / 127 (fp32, correctly rounded)
+// and code = round_half_away(value / scale), taken as one fused multiply-add
+// and a byte pick (code_rcp, code_bits in convrot_internal.h): the code is
+// the low byte of fma(v, rb, 1.5 * 2^23) with rb = RN(1 / scale) raised by
+// two units in the last place.  Exact ties round away from zero; a code
+// differs from the definition only where the exact quotient lies within
+// 2^-21 of a rounding boundary below it.  This takes 1.75 VALU instructions
+// per value (the fma and 3/4 of a byte permute), against 6.75 for a
+// correctly rounded quotient and rounding.  Scales below 2^-100 are lifted
+// by 2^64 with their values first.
 #include "convrot_internal.h"
 
 #include <cstdint>
@@ -95,23 +96,6 @@ __device__ __forceinline__ void fwht16_rest(float (&v)[16]) {
 // asm blocks, so the compiler would otherwise add NaN-quieting moves).
 __device__ __forceinline__ void max3_abs(float& m, float a, float b) {
   asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(m) : "v"(a), "v"(b));
-}
-
-// Byte-pack four int32 codes (each in [-127, 127]).
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-  const uint32_t lo = __builtin_amdgcn_perm(uint32_t(b), uint32_t(a), 0x0c0c0400u);  // a0 b0 0 0
-  const uint32_t hi = __builtin_amdgcn_perm(uint32_t(d), uint32_t(c), 0x0c0c0400u);  // c0 d0 0 0
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);                                   // a0 b0 c0 d0
-}
-
-// round_half_away(n / d) for the correctly rounded fp32 quotient, given
-// r = RN(1/d) (both may carry the same sign flip).
-__device__ __forceinline__ int quantize(float n, float d, float r) {
-  const float q0 = n * r;
-  const float e = __builtin_fmaf(-q0, d, n);
-  const float q1 = __builtin_fmaf(e, r, q0);
-  const float half = __uint_as_float((__float_as_uint(q1) & 0x80000000u) | 0x3effffffu);  // +-0.49999997
-  return int(q1 + half);  // v_cvt_i32_f32 truncates
 }
 
 template <int C, int TW, bool NORM>
@@ -309,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
     }
     float s = amax / 127.0f;  // scale of the unnormalised values
     float out_mul = 0.0625f;  // 1/sqrt(256), exact
-    if (s < 0x1p-100f && s > 0.f) {
+    if (s < kTinyScale && s > 0.f) {
       // Tiny row (the branch is uniform: amax is the token's).  Lift values
       // and scale by 2^64 so 1/s stays finite and the quotient identity
       // holds; for a normal s the quotients are exactly the unlifted ones.
@@ -320,19 +304,18 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       s = (amax * 0x1p64f) / 127.0f;
       out_mul = 0x1p-68f;
     }
-    const float r = s > 0.f ? 1.0f / s : 0.f;
-    const float ds = sgn * s, dr = sgn * r;  // fold the lane's sign into the quotient
+    const float dr = sgn * code_rcp(s);  // the lane's sign folded into the reciprocal
     if (tok < M) {
       if (wt == 0 && lane == 0) x_scale[tok] = s * out_mul;
       int8_t* out = xq + tok * K;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
         if (!slot_ok(j)) continue;  // past the row's end
-        int q[16];
+        uint32_t q[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) q[i] = quantize(v[j][i], ds, dr);
-        const u32x4 o = {pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
-                         pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+        for (int i = 0; i < 16; ++i) q[i] = code_bits(v[j][i], dr);
+        const u32x4 o = {pack4_lo(q[0], q[1], q[2], q[3]), pack4_lo(q[4], q[5], q[6], q[7]),
+                         pack4_lo(q[8], q[9], q[10], q[11]), pack4_lo(q[12], q[13], q[14], q[15])};
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + chunk_off(j)));
       }
     }
@@ -408,9 +391,9 @@ hipError_t launch_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* 
 // bit-0 butterfly fused with the unpack, then bits 1..3.  A row spreads over
 // L = 64 / RPW lanes of a wave (RPW rows per wave), lane l taking chunks
 // l, l + L, ..., so any multiple of 16 fits; RPW is chosen per K to waste
-// the fewest chunk slots.  Quantization is the group-256 kernel's (exact
-// quotient, half away from zero, tiny-row lift); 1/sqrt(16) = 1/4 is folded
-// into the scale.
+// the fewest chunk slots.  Quantization is the group-256 kernel's (one fma
+// and a byte pick, ties away from zero, tiny-row lift); 1/sqrt(16) = 1/4 is
+// folded into the scale.
 template <int G, int C, int RPW>
 __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                       int K, int8_t* __restrict__ xq,
@@ -468,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
     for (int off = L / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     float s = amax / 127.0f;                      // scale of the unnormalised values
     float out_mul = G == 16 ? 0.25f : 1.0f;       // 1/sqrt(G), exact
-    if (s < 0x1p-100f && s > 0.f) {
+    if (s < kTinyScale && s > 0.f) {
       // Tiny row (uniform over the row's lanes): lift by 2^64 as in the
       // group-256 kernel so 1/s stays finite and the quotient identity holds.
 #pragma unroll
@@ -478,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
       s = (amax * 0x1p64f) / 127.0f;
       out_mul *= 0x1p-64f;
     }
-    const float r = s > 0.f ? 1.0f / s : 0.f;
+    const float rb = code_rcp(s);
     if (tok < M) {
       if (l == 0) x_scale[tok] = s * out_mul;
       int8_t* out = xq + tok * K;
@@ -486,11 +469,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_small_kernel(const uint
       for (int j = 0; j < C; ++j) {
         const int c = l + L * j;
         if (c < nchunks) {
-          int q[16];
+          uint32_t q[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) q[i] = quantize(v[j][i], s, r);
-          const u32x4 o = {pack4(q[0], q[1], q[2], q[3]), pack4(q[4], q[5], q[6], q[7]),
-                           pack4(q[8], q[9], q[10], q[11]), pack4(q[12], q[13], q[14], q[15])};
+          for (int i = 0; i < 16; ++i) q[i] = code_bits(v[j][i], rb);
+          const u32x4 o = {pack4_lo(q[0], q[1], q[2], q[3]), pack4_lo(q[4], q[5], q[6], q[7]),
+                           pack4_lo(q[8], q[9], q[10], q[11]), pack4_lo(q[12], q[13], q[14], q[15])};
           __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + c * 16));
         }
       }
@@ -579,10 +562,12 @@ hipError_t launch_small_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, f
 // with the lane's known sign; the value s_w * (t * 2^-4) is rounded to bf16.
 // t * 2^-4 is formed as fma(v, sign * 2^-4, +0), exact, which also turns a
 // zero t into +0 as the plain transform gives it (a bare sign flip would
-// leave -0 there).  Groups never straddle rows (K is a
+// leave -0 there); the scale is applied as fma(s, ., +0) for the same
+// reason (a zero scale times a negative t would otherwise give -0, where
+// the dense product sums to +0).  Groups never straddle rows (K is a
 // multiple of 256), so the matrix is walked as a flat list of groups.
 // ("MOSS-Image Qwen3.5-9B text encoder, INT8 (W8A8, ConvRot)", file table
-// row "Matmul": the weight can be dequantized for a bf16 matmul.)
+// row "Matmul": its weight-only mode expands the codes into a bf16 weight.)
 template <bool W4>
 __global__ __launch_bounds__(kThreads) void dequant_g256_kernel(const void* __restrict__ wq,
                                                                 const float* __restrict__ w_scale, int64_t ngroups,
@@ -630,7 +615,8 @@ __global__ __launch_bounds__(kThreads) void dequant_g256_kernel(const void* __re
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    o[i] = pack_bf16x2(s * __builtin_fmaf(v[2 * i], sg, 0.0f), s * __builtin_fmaf(v[2 * i + 1], sg, 0.0f));
+    o[i] = pack_bf16x2(__builtin_fmaf(s, __builtin_fmaf(v[2 * i], sg, 0.0f), 0.0f),
+                       __builtin_fmaf(s, __builtin_fmaf(v[2 * i + 1], sg, 0.0f), 0.0f));
   u32x4* dst = reinterpret_cast<u32x4*>(out + grp * 256 + u * 16);
   dst[0] = u32x4{o[0], o[1], o[2], o[3]};
   dst[1] = u32x4{o[4], o[5], o[6], o[7]};
