@@ -83,8 +83,9 @@ enum convrot_status {
   CONVROT_ERR_WORKSPACE = 5, /* workspace smaller than the call's workspace-size function gives */
   CONVROT_ERR_DEVICE = 6,    /* the HIP runtime reported an error while enqueueing */
   CONVROT_ERR_DTYPE = 7,     /* unsupported w_dtype or bits value */
-  CONVROT_ERR_ARG = 8        /* a scalar argument is out of range (eps negative, NaN or infinite;
+  CONVROT_ERR_ARG = 8,       /* a scalar argument is out of range (eps negative, NaN or infinite;
                                 n_outs outside [1, CONVROT_MAX_OUTS]) */
+  CONVROT_ERR_SCRATCH = 9    /* the input needs more than the allocation-free call's scratch area */
 };
 
 /* Weight dtypes accepted by convrot_quantize_weight. */
@@ -296,6 +297,27 @@ int convrot_gemm_i8_multi(const int8_t *xq, const float *x_scale, int wbits, int
 int convrot_linear_multi(const uint16_t *x, int64_t M, int64_t K, int group, int wbits,
                          const convrot_linear_out *outs, int n_outs, void *workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/*
+ * convrot_w8a8_linear_noalloc -- convrot_w8a8_linear for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses that own every allocation.  It takes no
+ * workspace: the int8 codes and fp32 token scales of x go to a scratch area
+ * the library holds in device memory, CONVROT_NOALLOC_SCRATCH_BYTES per GPU
+ * (a file-scope device array, present on every GPU the library runs on until
+ * the process ends).  The call itself allocates nothing and calls no
+ * allocating routine; its first call on a GPU looks up that GPU's scratch
+ * address once.  Arguments, results and errors as convrot_w8a8_linear, and
+ * bit for bit the same output; an input whose convrot_workspace_size(M, K)
+ * exceeds CONVROT_NOALLOC_SCRATCH_BYTES returns CONVROT_ERR_SCRATCH before
+ * anything is enqueued.  Every call on one GPU shares that GPU's scratch
+ * area, so calls that overlap on one GPU (several streams or host threads)
+ * race: the caller serialises them.  Nothing in the area needs clearing
+ * between calls (each call writes every byte it reads).
+ */
+#define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int convrot_w8a8_linear_noalloc(const uint16_t *x, int64_t M, int64_t K, const int8_t *wq, const float *w_scale,
+                                int64_t N, int group, uint16_t *y, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *convrot_status_string(int status);

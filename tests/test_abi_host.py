@@ -43,7 +43,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings_and_version(L):
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert len(cr.convrot_status_string(s)) > 0
     assert "unknown" in cr.convrot_status_string(99)
     assert cr.convrot_version() >= 100
@@ -67,7 +67,7 @@ MIS = ctypes.c_void_p(0x10008)
 NUL = None
 S0 = ctypes.c_void_p(0)
 
-ERR = {"null": 1, "shape": 2, "group": 3, "align": 4, "ws": 5, "dtype": 7, "arg": 8}
+ERR = {"null": 1, "shape": 2, "group": 3, "align": 4, "ws": 5, "dtype": 7, "arg": 8, "scratch": 9}
 
 
 def rq(x, M, K, g, q, s):
@@ -251,3 +251,19 @@ def test_dequant_path_validation(L):
     assert dl(A, 8, 512, B, 8, NUL, 64, 256, D, E, need) == ERR["null"]
     assert dl(A, 8, 512, B, 8, C, 64, 256, D, MIS, need) == ERR["align"]
     assert dl(NUL, 0, 512, NUL, 8, NUL, 64, 256, NUL, NUL, 0) == 0
+
+
+def test_noalloc_validation(L):
+    """The allocation-free linear checks its arguments like the others and
+    refuses an input larger than its scratch area before any HIP call."""
+    na = lambda x, M, K, w, s, N, g, y: cr.load().convrot_w8a8_linear_noalloc(x, M, K, w, s, N, g, y, S0)
+    assert na(A, 8, 512, B, C, 0, 256, D) == ERR["shape"]
+    assert na(A, 8, 500, B, C, 64, 256, D) == ERR["shape"]
+    assert na(A, 8, 512, B, C, 64, 100, D) == ERR["group"]
+    assert na(A, 8, 512, NUL, C, 64, 256, D) == ERR["null"]
+    assert na(A, 8, 512, B, C, 64, 256, MIS) == ERR["align"]
+    assert na(NUL, 0, 512, NUL, NUL, 64, 256, NUL) == 0
+    K = 4096
+    M = cr.NOALLOC_SCRATCH_BYTES // K                 # the codes fill the area, the scales do not fit
+    assert cr.convrot_workspace_size(M, K) > cr.NOALLOC_SCRATCH_BYTES
+    assert na(A, M, K, B, C, 64, 256, D) == ERR["scratch"]

@@ -22,7 +22,7 @@ __all__ = [
     "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear", "convrot_w4a8_linear",
     "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi", "convrot_dequantize_weight",
     "convrot_gemm_bf16", "convrot_dequant_workspace_size", "convrot_dequant_linear",
-    "convrot_status_string", "convrot_version",
+    "convrot_w8a8_linear_noalloc", "convrot_status_string", "convrot_version", "NOALLOC_SCRATCH_BYTES",
     "quantize_weight", "rotate_quant", "rmsnorm_rotate_quant", "w8a8_linear", "w4a8_linear", "gemm_i8",
     "gemm_i8_multi", "linear_multi", "dequantize_weight", "gemm_bf16", "dequant_linear", "workspace",
 ]
@@ -35,6 +35,7 @@ OK = 0
 W_F32, W_BF16 = 0, 1
 MAX_K = 32768
 MAX_OUTS = 8
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LinearOut(ctypes.Structure):
@@ -79,6 +80,7 @@ def load():
         "convrot_gemm_bf16": (I, [P, P, I64, I64, I64, P, P]),
         "convrot_dequant_workspace_size": (SZ, [I64, I64]),
         "convrot_dequant_linear": (I, [P, I64, I64, P, I, P, I64, I, P, P, SZ, P]),
+        "convrot_w8a8_linear_noalloc": (I, [P, I64, I64, P, P, I64, I, P, P]),
         "convrot_status_string": (ctypes.c_char_p, [I]),
         "convrot_version": (I, []),
     }
@@ -96,7 +98,7 @@ def exported_symbols():
             "convrot_rmsnorm_rotate_quant", "convrot_workspace_size", "convrot_w8a8_linear",
             "convrot_w4a8_linear", "convrot_gemm_i8", "convrot_gemm_i8_multi", "convrot_linear_multi",
             "convrot_dequantize_weight", "convrot_gemm_bf16", "convrot_dequant_workspace_size",
-            "convrot_dequant_linear", "convrot_status_string", "convrot_version"]
+            "convrot_dequant_linear", "convrot_w8a8_linear_noalloc", "convrot_status_string", "convrot_version"]
 
 
 # ------------------------------------------------------------ marshalling
@@ -248,6 +250,16 @@ def convrot_w8a8_linear(x, M, K, wq, w_scale, N, group, y, workspace, workspace_
     _need_linear(x, M, K, wq, N * K, w_scale, N, y, workspace, workspace_bytes)
     return load().convrot_w8a8_linear(_dptr(x), int(M), int(K), _dptr(wq), _dptr(w_scale), int(N), int(group),
                                       _dptr(y), _dptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def convrot_w8a8_linear_noalloc(x, M, K, wq, w_scale, N, group, y, stream=None) -> int:
+    if M > 0 and K > 0 and N > 0:
+        _need(x, 2 * M * K, "x")
+        _need(wq, N * K, "wq")
+        _need(w_scale, 4 * N, "w_scale")
+        _need(y, 2 * M * N, "y")
+    return load().convrot_w8a8_linear_noalloc(_dptr(x), int(M), int(K), _dptr(wq), _dptr(w_scale), int(N),
+                                              int(group), _dptr(y), _stream(stream))
 
 
 def convrot_w4a8_linear(x, M, K, wq4, w_scale, N, group, y, workspace, workspace_bytes, stream=None) -> int:

@@ -5,6 +5,15 @@
 
 #include "convrot_internal.h"
 
+#include <mutex>
+
+// Scratch area of the allocation-free linear (convrot_w8a8_linear_noalloc):
+// the quantized activations and token scales.  Each GPU the library runs on
+// holds its own copy for the life of the process.  In host code this name
+// stands for the array but is not its device address: host code uses only
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[CONVROT_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -73,6 +82,22 @@ hipError_t launch_outs(const int8_t* xq, const float* xs, int wbits, int64_t M, 
   return convrot::launch_gemm_multi(xq, xs, wbits, M, K, d, n_outs, stream);
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; nullptr if the lookup failed.
+constexpr int kScratchDevices = 64;
+std::once_flag scratch_once[kScratchDevices];
+void* scratch_ptr[kScratchDevices];
+
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return nullptr;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +118,8 @@ const char* convrot_status_string(int status) {
     case CONVROT_ERR_DTYPE: return "unsupported weight dtype or bit width";
     case CONVROT_ERR_ARG: return "a scalar argument is out of range (eps negative or not finite, or n_outs "
                                  "outside [1, 8])";
+    case CONVROT_ERR_SCRATCH: return "input too large for the allocation-free call: convrot_workspace_size(M, K) "
+                                     "exceeds CONVROT_NOALLOC_SCRATCH_BYTES (64 MiB)";
     default: return "unknown convrot status";
   }
 }
@@ -196,6 +223,22 @@ int convrot_w8a8_linear(const uint16_t* x, int64_t M, int64_t K, const int8_t* w
                         int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   return linear_impl(x, M, K, wq, 8, w_scale, N, group, y, workspace, workspace_bytes, stream);
+}
+
+int convrot_w8a8_linear_noalloc(const uint16_t* x, int64_t M, int64_t K, const int8_t* wq, const float* w_scale,
+                                int64_t N, int group, uint16_t* y, hipStream_t stream) {
+  // Host checks first, in the order the other linears use; the size limit
+  // is checked before any HIP call.
+  if (int rc = check_k(K, group, false)) return rc;
+  if (M < 0 || N <= 0 || M > kMaxRows || N > kMaxRows || !tiles_fit(M, (N + 127) / 128))
+    return CONVROT_ERR_SHAPE;
+  if (M == 0) return CONVROT_OK;
+  if (!x || !wq || !w_scale || !y) return CONVROT_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(wq, 16) || !aligned(y, 16) || !aligned(w_scale, 4)) return CONVROT_ERR_ALIGN;
+  if (convrot_workspace_size(M, K) > CONVROT_NOALLOC_SCRATCH_BYTES) return CONVROT_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return CONVROT_ERR_DEVICE;
+  return linear_impl(x, M, K, wq, 8, w_scale, N, group, y, ws, CONVROT_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int convrot_w4a8_linear(const uint16_t* x, int64_t M, int64_t K, const uint8_t* wq4, const float* w_scale,
