@@ -9,15 +9,22 @@ epilogue) with all inputs resident in HBM.  Steps cycle through several
 buffer sets whose total exceeds twice the 256 MB Infinity Cache, so every
 step reads its operands from HBM.
 
+Order: the per-kernel timings of the roofline (GEMM alone, rotate-quantize
+alone, each after its own 50 ms of warm-up launches) run first, then the W
+untimed warm-up steps and the K timed steps of the headline, then seven
+more runs of at least 10 ms of steps (median and min), the parity check
+against the oracle, and the extras.
+
 Prints ONE JSON line on stdout: TOPS (2*M*N*K per step / step time), plus
 tokens/s, the GEMM kernel's roofline position (timed live with HIP events on
 the launch stream), the rotate-quantize kernel's HBM bandwidth (also fused
-with the preceding RMSNorm), and the CPU oracle timed on a bounded sample on
-this host.
+with the preceding RMSNorm), the parity of the benchmarked buffers against
+the oracle (every activation code of the input), and the CPU oracle timed
+on a bounded sample on this host (all threads and one, per stage).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                        [--no-extras]
-                       [--profile {gemm,gemm_bf16,rq,rq_large,rq_g16,rmsnorm_rq,copy,linear}]
+                       [--profile {gemm,gemm_tiles,gemm_bf16,rq,rq_large,rq_g16,rmsnorm_rq,copy,linear}]
 """
 from __future__ import annotations
 
@@ -138,12 +145,37 @@ def build_sets(torch, cr, wl, nsets):
     return x, w, sets
 
 
-def cpu_baseline(x, w, target_s=12.0):
+def host_cpu():
+    """The host the CPU baseline runs on: model name, logical CPUs, and the
+    CPUs this process may run on."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        allowed = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_allowed": allowed}
+
+
+def cpu_baseline(x, w, target_s=12.0, target_1t_s=3.0):
     """The CPU oracle as it stands, on the host cores: rotate+quantize a
     sample of tokens, naive int32 GEMM against all N rows, bf16 epilogue.
-    Weight preparation is offline (not timed), as on the GPU side."""
+    Weight preparation is offline (not timed), as on the GPU side.  The
+    value is the whole linear on all threads; the record adds the time of
+    each stage on the same sample (rotation alone, quantization as the
+    rest of the rotate-quantize call, GEMM, epilogue) and the whole linear
+    on one thread over a smaller sample (the cost is linear in tokens)."""
     import oracle
+    from w8a8_quantized_linear_amd import workloads as wl
     wq, ws = oracle.quantize_weight_i8(w, GROUP)
+    threads = oracle.num_threads()
     ms = 16
     t0 = time.perf_counter()
     oracle.w8a8_linear(np.ascontiguousarray(x[:ms]), wq, ws, GROUP)
@@ -156,47 +188,98 @@ def cpu_baseline(x, w, target_s=12.0):
     for _ in range(reps):
         oracle.w8a8_linear(xs, wq, ws, GROUP)
     t = (time.perf_counter() - t0) / reps
+
+    # Stages, once each, on the same sample and threads.
+    stages = {}
+    x64 = wl.bf16_bits_to_float(xs).astype(np.float64)
+    t0 = time.perf_counter()
+    oracle.rotate_rows(x64, GROUP)
+    stages["rotation"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    xq, xsc = oracle.rotate_quant(xs, GROUP)
+    stages["quantize"] = max(0.0, time.perf_counter() - t0 - stages["rotation"])
+    t0 = time.perf_counter()
+    acc = oracle.gemm_i8(xq, wq)
+    stages["gemm"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.epilogue(acc, xsc, ws)
+    stages["epilogue"] = time.perf_counter() - t0
+
+    # One thread, on a smaller sample.
+    oracle.set_num_threads(1)
+    try:
+        m1 = 2
+        t0 = time.perf_counter()
+        oracle.w8a8_linear(np.ascontiguousarray(x[:m1]), wq, ws, GROUP)
+        tp = time.perf_counter() - t0
+        m1 = int(min(ms, max(2, m1 * target_1t_s / max(tp, 1e-3))))
+        t0 = time.perf_counter()
+        oracle.w8a8_linear(np.ascontiguousarray(x[:m1]), wq, ws, GROUP)
+        t1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(threads)
     return {
         "value": 2.0 * ms * N * K / t / 1e12,
         "unit": "TOPS",
-        "cores": oracle.num_threads(),
+        "cores": threads,
         "kind": "oracle",
         "sample": f"first {ms} of {M} tokens, full K={K} x N={N} (GEMM cost is linear in tokens), "
                   f"{reps} repetition(s), {t * reps:.1f} s in total; weights quantized by the oracle "
                   f"beforehand (untimed)",
         "tokens_per_s": ms / t,
         "seconds": t * reps,
+        "host": host_cpu(),
+        "threads": threads,
+        "compile_flags": " ".join(["gcc", *oracle.CFLAGS]),
+        "stage_seconds": {k: round(v, 4) for k, v in stages.items()},
+        "stage_sample_tokens": ms,
+        "one_thread": {"tokens": m1, "seconds": round(t1, 3), "tokens_per_s": m1 / t1,
+                       "tops": 2.0 * m1 * N * K / t1 / 1e12},
     }
 
 
 def check_parity(torch, cr, x, w, y_dev, xq_dev, xs_dev, wq_dev, ws_dev):
-    """Sampled parity of the benchmarked buffers against the oracle, on 16
-    tokens x 128 weight rows: the activation and weight codes (fraction that
-    differ), the int32 accumulators of the GPU's own codes (exact or not)
-    and the bf16 output (relative L2)."""
+    """Parity of the benchmarked buffers against the oracle: every activation
+    code and scale of the input (M x K), the weight codes and scales of 1024
+    sampled rows, the int32 accumulators of the GPU's own codes on 64 tokens
+    x 1024 rows (exact or not), and the bf16 output on those pairs against
+    the oracle's (relative L2).  The oracle decides codes on the exact
+    rotation, so a few codes per million may differ by one at rounding
+    boundaries."""
     import oracle
     rng = np.random.default_rng(7)
-    toks = np.sort(rng.choice(M, 16, replace=False))
-    rows = np.sort(rng.choice(N, 128, replace=False))
-    xq, xs = oracle.rotate_quant(np.ascontiguousarray(x[toks]), GROUP)
-    wq, ws = oracle.quantize_weight_i8(np.ascontiguousarray(w[rows]), GROUP)
-    y_ref = oracle.epilogue(oracle.gemm_i8(xq, wq), xs, ws)
+    toks = np.sort(rng.choice(M, 64, replace=False))
+    rows = np.sort(rng.choice(N, 1024, replace=False))
+    xq_ref, xs_ref = oracle.rotate_quant(np.ascontiguousarray(x), GROUP)
+    wq_ref, ws_ref = oracle.quantize_weight_i8(np.ascontiguousarray(w[rows]), GROUP)
+    y_ref = oracle.epilogue(oracle.gemm_i8(xq_ref[toks], wq_ref), xs_ref[toks], ws_ref)
     y = y_dev.view(torch.int16).cpu().numpy().view(np.uint16)[np.ix_(toks, rows)]
     f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    xq_g = xq_dev.cpu().numpy()[toks]
+    xq_g = xq_dev.cpu().numpy()
+    xs_g = xs_dev.cpu().numpy()
     wq_g = wq_dev.cpu().numpy()[rows]
+    ws_g = ws_dev.cpu().numpy()[rows]
     # The GEMM on the GPU's own codes, all N, accumulators kept.
     acc = torch.empty((M, N), dtype=torch.int32, device=xq_dev.device)
     _ok(cr, cr.convrot_gemm_i8(xq_dev, xs_dev, wq_dev, 8, ws_dev, M, N, K, acc, None))
     torch.cuda.synchronize()
     acc_g = acc.cpu().numpy()[np.ix_(toks, rows)]
     del acc
+    dx = xq_g.astype(np.int16) - xq_ref
+    dw = wq_g.astype(np.int16) - wq_ref
+    rel = lambda a, b: float(np.max(np.abs(a.astype(np.float64) - b) / np.where(b == 0, 1, np.abs(b))))
     return {
-        "sample": "16 tokens x 128 weight rows",
+        "sample": f"activation codes: all {M} x {K}; weight codes: {rows.size} rows x {K}; "
+                  f"output and accumulators: {toks.size} tokens x {rows.size} rows",
         "rel_l2": float(np.linalg.norm(f(y) - f(y_ref)) / np.linalg.norm(f(y_ref))),
-        "code_mismatch_frac": float(np.mean(xq_g != xq)),
-        "weight_code_mismatch_frac": float(np.mean(wq_g != wq)),
-        "acc_exact": bool(np.array_equal(acc_g, oracle.gemm_i8(xq_g, wq_g))),
+        "code_mismatch_frac": float(np.count_nonzero(dx)) / dx.size,
+        "code_mismatch_count": int(np.count_nonzero(dx)),
+        "code_max_abs_diff": int(np.abs(dx).max()),
+        "weight_code_mismatch_frac": float(np.count_nonzero(dw)) / dw.size,
+        "weight_code_mismatch_count": int(np.count_nonzero(dw)),
+        "scale_max_rel_diff": rel(xs_g, xs_ref),
+        "weight_scale_max_rel_diff": rel(ws_g, ws_ref),
+        "acc_exact": bool(np.array_equal(acc_g, oracle.gemm_i8(xq_g[toks], wq_g))),
     }
 
 
@@ -482,9 +565,38 @@ def copy_peak(torch, timer):
             "elementwise": round(2 * (1 << 30) / t_ew / 1e9, 1)}
 
 
+# GEMM shapes whose tile plans the counter runs cover (M, N, K, weight bits):
+# the headline shape (256x192 tiles), the MLP down shape (256x128, three
+# stages), the attention shape M=512 (64x128, four stages) and M=4096,
+# N=12288 (256x256), int8 and int4 weights; each plan also at a second K, so
+# that counts which grow with K (the main loop) separate from those which do
+# not (set-up and epilogue).
+GEMM_TILE_SHAPES = [(2048, 12288, 4096, 8), (2048, 12288, 8192, 8), (2048, 4096, 12288, 8), (2048, 4096, 4096, 8),
+                    (512, 4096, 4096, 8), (512, 4096, 8192, 8), (4096, 12288, 4096, 8), (4096, 12288, 8192, 8),
+                    (2048, 12288, 4096, 4), (2048, 12288, 8192, 4), (2048, 4096, 12288, 4), (2048, 4096, 4096, 4),
+                    (512, 4096, 4096, 4), (512, 4096, 8192, 4), (4096, 12288, 4096, 4), (4096, 12288, 8192, 4)]
+
+
 def profile_mode(mode, torch, cr, wl):
     """Short runs for rocprofv3 counter collection (a handful of launches)."""
     dev = torch.device("cuda")
+    if mode == "gemm_tiles":
+        g = torch.Generator(device=dev).manual_seed(3)
+        for (m, n, k, bits) in GEMM_TILE_SHAPES:
+            xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=dev, generator=g)
+            if bits == 8:
+                wq = torch.randint(-127, 128, (n, k), dtype=torch.int8, device=dev, generator=g)
+            else:
+                wq = torch.randint(0, 256, (n, k // 2), dtype=torch.uint8, device=dev, generator=g)
+            xs = torch.rand(m, device=dev, generator=g) * 0.01
+            ws = torch.rand(n, device=dev, generator=g) * 0.01
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                _ok(cr, cr.convrot_gemm_i8(xq, xs, wq, bits, ws, m, n, k, None, y))
+            torch.cuda.synchronize()
+            log(f"profile mode gemm_tiles: W{bits} M={m} N={n} K={k}, 3 launches")
+            del xq, wq, xs, ws, y
+        return
     if mode == "copy":
         n = 1 << 30
         a = torch.empty((n,), dtype=torch.uint8, device=dev)
@@ -559,7 +671,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "gemm_bf16", "rq", "rq_large", "rq_g16", "rmsnorm_rq", "copy", "linear"], default=None)
+    ap.add_argument("--profile", choices=["gemm", "gemm_tiles", "gemm_bf16", "rq", "rq_large", "rq_g16", "rmsnorm_rq",
+                                          "copy", "linear"], default=None)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -590,6 +703,24 @@ def main():
         xd, wq, ws, y, wsp = sets[i % nsets]
         cr.w8a8_linear(xd, wq, ws, group=GROUP, out=y, ws=wsp)
 
+    ops = 2.0 * M * N * K
+    # Per-kernel durations, live, on the launch stream (each after its own
+    # 50 ms of warm-up launches).  They run before the headline region, so
+    # the headline's steps start on a device that has been under this load.
+    q = [cr.rotate_quant(s[0]) for s in sets]
+    t_gemm = timer.time(lambda i: cr.convrot_gemm_i8(q[i % nsets][0], q[i % nsets][1], sets[i % nsets][1], 8,
+                                                     sets[i % nsets][2], M, N, K, None, sets[i % nsets][3]),
+                        max(200, args.steps))
+    t_rq = timer.time(lambda i: cr.convrot_rotate_quant(sets[i % nsets][0], M, K, GROUP, q[i % nsets][0],
+                                                        q[i % nsets][1]), max(200, args.steps))
+    # resident (hot) variant of the whole step, for reference
+    t_hot = timer.time(lambda i: cr.w8a8_linear(sets[0][0], sets[0][1], sets[0][2], out=sets[0][3],
+                                                ws=sets[0][4]), max(200, args.steps))
+    gemm_tops = ops / t_gemm / 1e12
+    rq_bytes = M * (3 * K + 4)
+    rq_gbs = rq_bytes / t_rq / 1e9
+
+    # The headline: W untimed warm-up steps, then exactly K timed steps.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -604,37 +735,22 @@ def main():
     wall = time.perf_counter() - t0
     t_step = start.elapsed_time(end) / 1e3 / args.steps
     log(f"timed {args.steps} steps: {t_step * 1e6:.1f} us/step (host wall {wall * 1e3:.1f} ms)")
-
-    ops = 2.0 * M * N * K
     tops = ops / t_step / 1e12
 
-    # Five more timed runs of the same steps (after the headline region, so
-    # they do not affect it): the spread of the per-step time.
+    # Seven more timed runs (after the headline region, so they do not
+    # affect it), each of at least 10 ms of steps: median and min per step.
+    rep_steps = max(args.steps, int(np.ceil(0.010 / max(t_step, 1e-6))))
     reps = []
-    for r in range(5):
+    for r in range(7):
         s0 = torch.cuda.Event(enable_timing=True)
         s1 = torch.cuda.Event(enable_timing=True)
         s0.record()
-        for i in range(args.steps):
+        for i in range(rep_steps):
             step(i)
         s1.record()
         s1.synchronize()
-        reps.append(s0.elapsed_time(s1) / args.steps)
+        reps.append(s0.elapsed_time(s1) / rep_steps)
     reps.sort()
-
-    # Per-kernel durations, live, on the launch stream.
-    q = [cr.rotate_quant(s[0]) for s in sets]
-    t_gemm = timer.time(lambda i: cr.convrot_gemm_i8(q[i % nsets][0], q[i % nsets][1], sets[i % nsets][1], 8,
-                                                     sets[i % nsets][2], M, N, K, None, sets[i % nsets][3]),
-                        max(50, args.steps))
-    t_rq = timer.time(lambda i: cr.convrot_rotate_quant(sets[i % nsets][0], M, K, GROUP, q[i % nsets][0],
-                                                        q[i % nsets][1]), max(50, args.steps))
-    # resident (hot) variant of the whole step, for reference
-    t_hot = timer.time(lambda i: cr.w8a8_linear(sets[0][0], sets[0][1], sets[0][2], out=sets[0][3],
-                                                ws=sets[0][4]), max(50, args.steps))
-    gemm_tops = ops / t_gemm / 1e12
-    rq_bytes = M * (3 * K + 4)
-    rq_gbs = rq_bytes / t_rq / 1e9
 
     last = sets[(args.steps - 1) % nsets]
     parity = check_parity(torch, cr, x, w, last[3], *q[(args.steps - 1) % nsets], last[1], last[2])
@@ -664,8 +780,10 @@ def main():
         "tokens_per_s": round(M / t_step, 1),
         "pct_int8_peak": round(tops / PEAK_INT8_TOPS, 4),
         "hot_tops": round(ops / t_hot / 1e12, 2),
-        "step_repeats": {"runs": len(reps), "steps_each": args.steps, "median_ms": round(reps[len(reps) // 2], 5),
-                         "min_ms": round(reps[0], 5), "max_ms": round(reps[-1], 5)},
+        "step_repeats": {"runs": len(reps), "steps_each": rep_steps, "median_ms": round(reps[len(reps) // 2], 5),
+                         "min_ms": round(reps[0], 5), "max_ms": round(reps[-1], 5),
+                         "median_tops": round(ops / (reps[len(reps) // 2] * 1e-3) / 1e12, 2),
+                         "max_tops": round(ops / (reps[0] * 1e-3) / 1e12, 2)},
         "roofline": {
             "bound": "mfma",
             "kernel": "gemm_i8_k128_kernel (int8 MFMA GEMM + bf16 epilogue)",
