@@ -42,6 +42,21 @@ def test_every_declared_symbol_is_exported(L):
     assert sorted(cr.exported_symbols()) == declared_functions()
 
 
+def test_library_reads_no_environment():
+    """The library as built takes no settings from the environment: the
+    tile-forcing overrides exist only in tuning builds (-DCONVROT_TUNING)."""
+    import shutil
+    import subprocess
+    lib = cr.library_path()
+    if not os.path.exists(lib):
+        pytest.skip("libconvrot.so not built (run __graft_entry__.build())")
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True, check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    assert not imported & {"getenv", "secure_getenv"}, "the library reads environment variables"
+
+
 def test_status_strings_and_version(L):
     for s in range(0, 10):
         assert len(cr.convrot_status_string(s)) > 0

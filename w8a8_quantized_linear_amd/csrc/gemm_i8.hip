@@ -725,37 +725,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
   gemm_k128_body<BM, BN, false, EVEN, false, true, NS>(X, nullptr, M, K, tiles_m, tiles_n, outs);
 }
 
-// Workgroups of `kernel` the current device runs at once: compute units x
+// Workgroups of kernel K the current device runs at once: compute units x
 // resident workgroups per unit, a multiple of 8 on MI355X (256 units, one or
-// two per unit), so the persistent tile order stays XCD-aware.  Memoised per
-// device and kernel (a read-only fact of the device, guarded for calls from
-// several host threads); 0 on error.
-int resident_slots(const void* kernel) {
-  struct Entry {
-    const void* kernel;
-    int device, slots;
-  };
-  static std::mutex mu;
-  // Room for every persistent kernel here (int8, int4, multi-output and
-  // bf16 variants: 40) on several devices; past that the answer is
-  // recomputed on each call, which is correct but slower.
-  constexpr int kEntries = 256;
-  static Entry cache[kEntries];
-  static int used = 0;
+// two per unit), so the persistent tile order stays XCD-aware.  A read-only
+// fact of the device, worked out once per device and kernel (the first call
+// with that device current; later calls from any host thread only read it);
+// 0 on error.
+template <auto K>
+int resident_slots() {
+  constexpr int kDevices = 64;
+  static std::once_flag once[kDevices];
+  static int slots[kDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    for (int i = 0; i < used; ++i)
-      if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].slots;
-  }
-  int cus = 0, per_cu = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess) return 0;
-  const int slots = cus * (per_cu > 0 ? per_cu : 1);
-  std::lock_guard<std::mutex> lock(mu);
-  if (used < kEntries) cache[used++] = {kernel, dev, slots};
-  return slots;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  auto query = [](int d) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(K), kThreads, 0) !=
+        hipSuccess)
+      return 0;
+    return cus * (per_cu > 0 ? per_cu : 1);
+  };
+  if (dev >= kDevices) return query(dev);  // not memoised
+  std::call_once(once[dev], [&] { slots[dev] = query(dev); });
+  return slots[dev];
 }
 
 // One launch over the outputs in `d` (each a weight matrix with its
@@ -775,18 +768,20 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, con
   }
   const int tiles_m = (M + BM - 1) / BM;
   using Kernel = void (*)(const int8_t*, const float*, int, int, int, int, GemmOuts);
+  constexpr Kernel k_multi = gemm_i8_k128_kernel<BM, BN, W4, true, NS>;
+  constexpr Kernel k_multi_tail = gemm_i8_k128_tail_kernel<BM, BN, W4, true, NS>;
+  constexpr Kernel k_one = gemm_i8_k128_kernel<BM, BN, W4, false, NS>;
+  constexpr Kernel k_one_tail = gemm_i8_k128_tail_kernel<BM, BN, W4, false, NS>;
   const bool even = K % 256 == 0;
-  Kernel kernel = n > 1 ? (even ? gemm_i8_k128_kernel<BM, BN, W4, true, NS>
-                               : gemm_i8_k128_tail_kernel<BM, BN, W4, true, NS>)
-                        : (even ? gemm_i8_k128_kernel<BM, BN, W4, false, NS>
-                               : gemm_i8_k128_tail_kernel<BM, BN, W4, false, NS>);
+  const Kernel kernel = n > 1 ? (even ? k_multi : k_multi_tail) : (even ? k_one : k_one_tail);
   // Persistent configurations: as many workgroups as the device holds at
   // once (never more than there are tiles), each walking its tiles in turn;
   // otherwise one workgroup per tile.
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   int64_t slots = tiles;
   if (CfgK<BM, BN, W4, NS>::PERSIST) {
-    slots = resident_slots(reinterpret_cast<const void*>(kernel));
+    slots = n > 1 ? (even ? resident_slots<k_multi>() : resident_slots<k_multi_tail>())
+                  : (even ? resident_slots<k_one>() : resident_slots<k_one_tail>());
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
   }
   const dim3 grid(unsigned(tiles < slots ? tiles : slots));
@@ -799,12 +794,13 @@ struct TileChoice {
   int ns = 2;  // pipeline stages
 };
 
-// CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>] forces one of the tile shapes above
-// (the deeper pipelines: 256x128x3, 128x256x3, 128x128x3, 128x128x4,
-// 64x128x4, 128x64x4 for int8 and int4 weights, the first, fourth and fifth
-// for bf16; a tuning override for sweeps: every choice gives bit-identical
-// results).
+// Tuning builds only (-DCONVROT_TUNING): CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>]
+// forces one of the tile shapes above (the deeper pipelines: 256x128x3,
+// 128x256x3, 128x128x3, 128x128x4, 64x128x4, 128x64x4 for int8 and int4
+// weights, the first, fourth and fifth for bf16), for sweeps: every choice
+// gives bit-identical results.  The library as built reads no environment.
 TileChoice tile_override() {
+#ifdef CONVROT_TUNING
   static const TileChoice forced = [] {
     TileChoice t{0, 0};
     if (const char* s = getenv("CONVROT_GEMM_TILE")) {
@@ -815,6 +811,9 @@ TileChoice tile_override() {
     return t;
   }();
   return forced;
+#else
+  return TileChoice{0, 0};
+#endif
 }
 
 // A plan for int8 weights: up to two bands of output columns, each with its
@@ -844,22 +843,18 @@ struct Plan {
 // several outputs the tiles of all of them count, and 256x256 needs every
 // output's N to be a multiple of 256.
 // Compute units of the current device (256 on MI355X; fewer on a
-// partitioned device), memoised per device; 256 if the query fails.
+// partitioned device), queried once per device; 256 if the query fails.
 int device_cus() {
   constexpr int kDevices = 64;
-  static std::mutex mu;
-  static int cache[kDevices] = {};
+  static std::once_flag once[kDevices];
+  static int cus[kDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevices) return 256;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (cache[dev] > 0) return cache[dev];
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  cache[dev] = cus;
-  return cus;
+  std::call_once(once[dev], [dev] {
+    int c = 0;
+    cus[dev] = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && c > 0 ? c : 256;
+  });
+  return cus[dev];
 }
 
 TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
@@ -890,10 +885,11 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   return {128, 128};
 }
 
-// CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan for a
-// single output (a tuning override for sweeps; every plan gives
-// bit-identical results).
+// Tuning builds only (-DCONVROT_TUNING):
+// CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan for a single
+// output, for sweeps (every plan gives bit-identical results).
 bool plan_override(Plan& out) {
+#ifdef CONVROT_TUNING
   static const Plan forced = [] {
     Plan p{0, {{0, {0, 0}}, {0, {0, 0}}}};
     const char* s = getenv("CONVROT_GEMM_PLAN");
@@ -906,6 +902,10 @@ bool plan_override(Plan& out) {
   if (forced.nb == 0) return false;
   out = forced;
   return true;
+#else
+  (void)out;
+  return false;
+#endif
 }
 
 template <bool W4>
@@ -959,12 +959,14 @@ hipError_t launch_bf16(const uint16_t* x, const uint16_t* w, int M, int N, int K
   const int kbytes = 2 * K;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   using Kernel = void (*)(const int8_t*, int, int, int, int, GemmOuts);
-  const Kernel kernel =
-      kbytes % 256 == 0 ? gemm_bf16_k64_kernel<BM, BN, true, NS> : gemm_bf16_k64_kernel<BM, BN, false, NS>;
+  constexpr Kernel k_even = gemm_bf16_k64_kernel<BM, BN, true, NS>;
+  constexpr Kernel k_any = gemm_bf16_k64_kernel<BM, BN, false, NS>;
+  const bool even = kbytes % 256 == 0;
+  const Kernel kernel = even ? k_even : k_any;
   const int64_t tiles = int64_t(tiles_m) * tiles_n;
   int64_t slots = tiles;
   if (CfgK<BM, BN, false, NS>::PERSIST) {
-    slots = resident_slots(reinterpret_cast<const void*>(kernel));
+    slots = even ? resident_slots<k_even>() : resident_slots<k_any>();
     if (slots <= 0) return hipErrorInvalidDeviceFunction;
   }
   const dim3 grid(unsigned(tiles < slots ? tiles : slots));

@@ -524,8 +524,9 @@ hipError_t launch_small_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, f
     best_rpw = rpw;
     best_c = int(c);
   }
-  // CONVROT_RQ_SMALL_RPW=<1|2|4> forces the rows per wave (a tuning override
-  // for sweeps; every choice gives identical results) when it fits.
+#ifdef CONVROT_TUNING
+  // Tuning builds only: CONVROT_RQ_SMALL_RPW=<1|2|4> forces the rows per wave
+  // when it fits, for sweeps (every choice gives identical results).
   static const int forced_rpw = [] {
     const char* e = getenv("CONVROT_RQ_SMALL_RPW");
     return e ? atoi(e) : 0;
@@ -537,6 +538,7 @@ hipError_t launch_small_k(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, f
       best_c = int(c);
     }
   }
+#endif
 #define CONVROT_SMALL(RPW_)                                                        \
   switch (best_c) {                                                                \
     case 1: return launch_small<G, 1, RPW_>(x, M, K, xq, xs, stream);              \
