@@ -480,7 +480,12 @@ def extras_vision(torch, cr, wl, timer):
 
 def rq_passes(torch, cr, timer):
     """Rotate-quantize bandwidth on the large passes, each cycled through
-    enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16)."""
+    enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16).  Beside
+    each, a plain streaming pass over the same input buffers: torch's
+    vectorized elementwise kernel (x + 0 on the bf16 bits read as int32
+    words) into a buffer of the same size, 2 bytes read and 2 written per
+    value with no arithmetic: the rate a plain elementwise kernel reaches at
+    that size."""
     dev = torch.device("cuda")
     res = []
     for (m, k) in RQ_PASSES:
@@ -491,9 +496,15 @@ def rq_passes(torch, cr, timer):
         qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
         ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
         t = timer.time(lambda i: cr.convrot_rotate_quant(xs[i % n], m, k, GROUP, qs[i % n], ss[i % n]), 200, warm=50)
+        del qs, ss
+        ys = [torch.empty((m, k // 2), dtype=torch.int32, device=dev) for _ in range(n)]
+        t_ref = timer.time(lambda i: torch.add(xs[i % n].view(torch.int32), 0, out=ys[i % n]), 200, warm=50)
+        ref_bytes = 4 * m * k
         res.append({"M": m, "K": k, "us": round(t * 1e6, 2), "bytes": per,
-                    "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4)})
-        del xs, qs, ss
+                    "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4),
+                    "elementwise_same_input": {"us": round(t_ref * 1e6, 2), "bytes": ref_bytes,
+                                               "achieved": round(ref_bytes / t_ref / 1e9, 1)}})
+        del xs, ys
     return res
 
 
