@@ -539,6 +539,49 @@ def rmsnorm_rq_pass(torch, cr, wl, timer):
     return res
 
 
+def _mfma_probe(torch):
+    """The MFMA-rate helper (tests/gpu_probe/mfma_rate.hip, built by
+    __graft_entry__.build): a launcher for blocks x 256 threads."""
+    import ctypes
+    path = os.path.join(ROOT, "tests", "gpu_probe", "libmfma_rate.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_rate_launch.restype = ctypes.c_int
+    blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+
+    def run(iters):
+        rc = lib.mfma_rate_launch(blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc:
+            raise RuntimeError(f"mfma_rate_launch failed: {rc}")
+    return run, out, blocks
+
+
+MFMA_LOOP_ITERS = 10000
+
+
+def mfma_loop(torch, timer):
+    """Context for the roofline: the int8 rate of waves that do nothing but
+    v_mfma_i32_32x32x32_i8 (no memory traffic), two workgroups of four
+    waves per CU, about 2 ms per launch, timed like the kernels above."""
+    probe = _mfma_probe(torch)
+    if probe is None:
+        return {"error": "tests/gpu_probe/libmfma_rate.so not built"}
+    run, out, blocks = probe
+    run(1)
+    s1 = out.clone()
+    run(2)
+    consistent = bool(torch.equal(out, s1 * 2))
+    t = timer.time(lambda i: run(MFMA_LOOP_ITERS), 5, warm=1)
+    ops = blocks * 4 * MFMA_LOOP_ITERS * 8 * 65536
+    return {"workload": f"{blocks} workgroups x 4 waves x {MFMA_LOOP_ITERS} x 8 v_mfma_i32_32x32x32_i8",
+            "us": round(t * 1e6, 1), "tops": round(ops / t / 1e12, 1),
+            "frac": round(ops / t / 1e12 / PEAK_INT8_TOPS, 4), "work_doubles_with_iters": consistent}
+
+
 def device_info(torch):
     p = torch.cuda.get_device_properties(0)
     return {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
@@ -588,11 +631,20 @@ GEMM_TILE_SHAPES = [(2048, 12288, 4096, 8), (2048, 12288, 8192, 8), (2048, 4096,
                     (512, 4096, 4096, 4), (512, 4096, 8192, 4), (4096, 12288, 4096, 4), (4096, 12288, 8192, 4)]
 
 
+# Warm-up launches ahead of the profiled ones in --profile gemm_tiles (of the
+# first shape, about 50 ms) and --profile mfma_rate (about 60 ms): counters
+# taken on a device fresh from idle read a lower clock than the bench's
+# steady state.
+PROFILE_WARM_GEMM = 500
+PROFILE_WARM_MFMA = 20
+
+
 def profile_mode(mode, torch, cr, wl):
     """Short runs for rocprofv3 counter collection (a handful of launches)."""
     dev = torch.device("cuda")
     if mode == "gemm_tiles":
         g = torch.Generator(device=dev).manual_seed(3)
+        first = True
         for (m, n, k, bits) in GEMM_TILE_SHAPES:
             xq = torch.randint(-127, 128, (m, k), dtype=torch.int8, device=dev, generator=g)
             if bits == 8:
@@ -602,11 +654,26 @@ def profile_mode(mode, torch, cr, wl):
             xs = torch.rand(m, device=dev, generator=g) * 0.01
             ws = torch.rand(n, device=dev, generator=g) * 0.01
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            if first:  # the device's clock settles under tens of ms of load
+                for _ in range(PROFILE_WARM_GEMM):
+                    _ok(cr, cr.convrot_gemm_i8(xq, xs, wq, bits, ws, m, n, k, None, y))
+                first = False
             for _ in range(3):
                 _ok(cr, cr.convrot_gemm_i8(xq, xs, wq, bits, ws, m, n, k, None, y))
             torch.cuda.synchronize()
             log(f"profile mode gemm_tiles: W{bits} M={m} N={n} K={k}, 3 launches")
             del xq, wq, xs, ws, y
+        return
+    if mode == "mfma_rate":
+        probe = _mfma_probe(torch)
+        if probe is None:
+            raise SystemExit("bench.py: tests/gpu_probe/libmfma_rate.so not built")
+        run, _, blocks = probe
+        for _ in range(PROFILE_WARM_MFMA + 3):
+            run(MFMA_LOOP_ITERS)
+        torch.cuda.synchronize()
+        log(f"profile mode mfma_rate: {PROFILE_WARM_MFMA} warm-up and 3 launches of {blocks} x 4 waves x "
+            f"{MFMA_LOOP_ITERS} x 8 MFMAs")
         return
     if mode == "copy":
         n = 1 << 30
@@ -682,7 +749,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
-    ap.add_argument("--profile", choices=["gemm", "gemm_tiles", "gemm_bf16", "rq", "rq_large", "rq_g16", "rmsnorm_rq",
+    ap.add_argument("--profile", choices=["gemm", "gemm_tiles", "gemm_bf16", "rq", "rq_large", "rq_g16", "rmsnorm_rq", "mfma_rate",
                                           "copy", "linear"], default=None)
     args = ap.parse_args()
 
@@ -827,6 +894,8 @@ def main():
     log("fused RMSNorm + rotate-quantize M=8704 K=4096")
     out["rmsnorm_rotate_quant"] = rmsnorm_rq_pass(torch, cr, wl, timer)
     if not args.no_extras:
+        log("extras: MFMA-only loop for context")
+        out["mfma_loop"] = mfma_loop(torch, timer)
         log("extras: vendor int8 GEMM for context")
         try:
             out["vendor_int_mm"] = vendor_int_mm(torch, cr, wl, timer)
