@@ -37,12 +37,13 @@
 // stage in flight: such tiles run three stages (256x128) or four (128x128,
 // 64x128), each sent two or three steps ahead (template parameter NS).
 //
-// Why these choices: under sustained load this GEMM runs below the chip's top
-// clock, and the clock it holds rises when less data moves per MFMA (an
-// MFMA-only loop holds ~2.27 GHz; removing the global->LDS loads from this
-// kernel gives +25 % throughput at the same power, removing the LDS reads
-// +6 %).  So the largest tile that fills the machine wins (see choose_tile),
-// and per-load instruction overhead matters as much as bandwidth.
+// Why these choices: under sustained load the device holds a shader clock
+// well below its 2.4 GHz peak, about 1.75 GHz under a loop of nothing but
+// MFMAs and about 1.45 GHz under this GEMM's main loop, where the MFMA pipe
+// is busy 86-91 % of the cycles (rocprofv3 counters).  Feeding the MFMAs
+// costs clock more than it costs cycles, so the largest tile that fills the
+// machine (the fewest bytes moved per MFMA) wins (see choose_tile), and
+// per-load instruction overhead matters as much as bandwidth.
 //
 // LDS layouts, chosen by measuring ds_read_b128 throughput for these exact
 // fragment patterns (about 240 B/clk per CU conflict-free, against about 140
@@ -828,10 +829,11 @@ struct Plan {
   Band b[2];
 };
 
-// Tile plan, from measurements on MI355X under sustained load.  The chip
-// runs this GEMM below its top clock, and the clock rises when less data
-// moves per MFMA, so the largest tile (256x256: fewest L2->LDS bytes per
-// operation) wins once it fills several whole rounds of the CUs;
+// Tile plan, from measurements on MI355X under sustained load.  The device
+// holds a lower clock under this GEMM than under MFMAs alone (feeding them
+// costs power), so the largest tile (256x256: fewest L2->LDS bytes per
+// operation, its main loop 91 % MFMA-busy against 86 % for 256x192) wins
+// once it fills several whole rounds of the CUs;
 // otherwise 256x192 when it fills at least three quarters of a round, and
 // 128x128 for small problems (more CUs busy).  With a short K (fewer than 16
 // stages of 128 bytes per token row) a tile's set-up and epilogue weigh as
