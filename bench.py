@@ -583,9 +583,23 @@ def mfma_loop(torch, timer):
 
 
 def device_info(torch):
+    """Device name, architecture, CUs, HBM, the peak shader clock and the HIP
+    runtime version (from the runtime itself), torch's build."""
+    import ctypes
     p = torch.cuda.get_device_properties(0)
-    return {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+    info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
             "hbm_gib": round(p.total_memory / 2**30, 1), "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (hip_runtime_api.h): peak clock in kHz
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, torch.cuda.current_device()) == 0:
+            info["peak_clock_mhz"] = v.value / 1000
+        if hip.hipRuntimeGetVersion(ctypes.byref(v)) == 0:
+            info["hip_runtime_version"] = v.value
+    except OSError:
+        pass
+    return info
 
 
 def vendor_int_mm(torch, cr, wl, timer):
