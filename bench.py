@@ -329,6 +329,33 @@ def extras_configs(torch, cr, wl, timer):
     return res
 
 
+def extras_shards(torch, cr, wl, timer, x, w):
+    """One GPU's share of the headline linear under 8-way sharding, from
+    the headline's own inputs (cold buffer sets, one convrot_w8a8_linear
+    per launch): tensor-parallel over N (all 2048 tokens, 1536 of the 12288
+    weight rows) and data-parallel over M (256 of the 2048 tokens, all
+    rows).  Neither needs any exchange for the linear itself."""
+    dev = torch.device("cuda")
+    res = {}
+    for key, m0, m1, n0, n1 in (("tp8_N1536", 0, M, 0, N // 8), ("dp8_M256", 0, M // 8, 0, N)):
+        xs = np.ascontiguousarray(x[m0:m1])
+        wsl = np.ascontiguousarray(w[n0:n1])
+        mm, nn = m1 - m0, n1 - n0
+        wq, ws = cr.quantize_weight(torch.from_numpy(wsl).to(dev), group=GROUP, bits=8)
+        xd = torch.from_numpy(xs.view(np.int16)).to(dev).view(torch.bfloat16)
+        per = mm * K * 2 + nn * K + 2 * mm * nn
+        n = min(64, max(2, -(-2 * MALL_BYTES // per) + 1))
+        sets = [(xd.clone(), wq.clone(), ws.clone(), torch.empty((mm, nn), dtype=torch.bfloat16, device=dev),
+                 cr.workspace(mm, K, dev)) for _ in range(n)]
+        t = timer.time(lambda i: cr.w8a8_linear(*sets[i % n][:3], group=GROUP, out=sets[i % n][3],
+                                                ws=sets[i % n][4]), 200)
+        ops = 2.0 * mm * nn * K
+        res[key] = {"M": mm, "K": K, "N": nn, "us": round(t * 1e6, 2), "tops": round(ops / t / 1e12, 1),
+                    "tokens_per_s": round(mm / t, 1), "buffer_sets": n}
+        del sets, wq, ws, xd
+    return res
+
+
 def _ok(cr, rc):
     if rc != 0:
         raise RuntimeError(f"convrot status {rc}: {cr.convrot_status_string(rc)}")
@@ -917,6 +944,8 @@ def main():
             out["vendor_int_mm"] = {"error": str(e)[:200]}
         log("extras: single linears M=16 / 512 / 2048 (K 12288)")
         out["other_linears"] = extras_configs(torch, cr, wl, timer)
+        log("extras: one GPU's share of the headline linear under 8-way sharding")
+        out["shards"] = extras_shards(torch, cr, wl, timer, x, w)
         log("extras: W4A8 M=4096 K=4096 N=12288")
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
         log("extras: weight-only path M=2048 K=4096 N=12288")
