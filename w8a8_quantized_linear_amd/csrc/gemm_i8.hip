@@ -39,8 +39,8 @@
 //
 // Why these choices: under sustained load the device holds a shader clock
 // well below its 2.4 GHz peak, about 1.75 GHz under a loop of nothing but
-// MFMAs and about 1.45 GHz under this GEMM's main loop, where the MFMA pipe
-// is busy 86-91 % of the cycles (rocprofv3 counters).  Feeding the MFMAs
+// MFMAs and about 1.45-1.50 GHz under this GEMM's main loop, where the MFMA
+// pipe is busy 85-91 % of the cycles (rocprofv3 counters).  Feeding the MFMAs
 // costs clock more than it costs cycles, so the largest tile that fills the
 // machine (the fewest bytes moved per MFMA) wins (see choose_tile), and
 // per-load instruction overhead matters as much as bandwidth.
@@ -113,9 +113,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // MFMA from the start of the phase (so they have completed by the wait that
 // ends it), the NV buffer loads are spread evenly over the whole phase (so
 // the load path never sees a burst); a full scheduling barrier closes it.
-template <int NM, int NV, int ND>
+template <int NM, int NV, int ND, int NA = 0>
 __device__ __forceinline__ void interleave_phase() {
   int nv = 0;
+  // NA > 0: that many VALU instructions (the unpack of int4 weight
+  // fragments read in this phase) go after the second half of the MFMAs,
+  // when their LDS reads have landed; placed by the compiler they sat right
+  // after the reads and stalled the MFMA issue on the LDS latency (same-box
+  // A/B, bit-identical output: M 4096, N 12288, K 4096 163.7 -> 160.5 us,
+  // M 2048, N 12288, K 4096 85.1 -> 83.9 us; the deeper-pipeline small tiles
+  // measured no gain and keep NA = 0).
+  constexpr int H = NM / 2;
+  constexpr int PER = NA > 0 ? (NA + (NM - H) - 1) / (NM - H) : 0;
 #pragma unroll
   for (int i = 0; i < NM; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -125,9 +134,11 @@ __device__ __forceinline__ void interleave_phase() {
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       ++nv;
     }
+    if (NA > 0 && i >= H) __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
   }
   for (int i = NM; i < ND; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   for (; nv < NV; ++nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  if (NA > 0) __builtin_amdgcn_sched_group_barrier(0x002, NA, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -423,6 +434,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
   // LDS reads when fetching an even / odd slice (int4 weights are read once
   // per slice pair).
   constexpr int NM = C::NM, ND0 = TI + TJ, ND1 = W4 ? TJ : TI + TJ;
+  constexpr int NA = W4 ? 10 * TI : 0;  // unpack VALU per slice of int4 weights (two-stage loop)
   const int ksteps = EVEN ? K / 128 : ((K + 127) / 128 + 1) & ~1;  // even: the loop body covers two steps
 
   // Epilogue staging: a dedicated LDS area when it fits beside the stage
@@ -518,13 +530,13 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         read(s, 1, 1);
         mfma(0);
         issue(s ^ 1, (kt + 1) * 128, IP2{}, IL{});
-        interleave_phase<NM, C::G0, ND1>();
+        interleave_phase<NM, C::G0, ND1, NA>();
         read(s, 2, 0);
         mfma(1);
-        interleave_phase<NM, 0, ND0>();
+        interleave_phase<NM, 0, ND0, NA>();
         read(s, 3, 1);
         mfma(0);
-        interleave_phase<NM, 0, ND1>();
+        interleave_phase<NM, 0, ND1, NA>();
         wait_vmcnt<0>();
         sync_stage();
         __builtin_amdgcn_sched_barrier(0);
@@ -532,7 +544,7 @@ __device__ __forceinline__ void gemm_k128_body(const int8_t* __restrict__ X, con
         issue(s, (kt + 2) * 128, I0{}, IP2{});
         read(s ^ 1, 0, 0);
         mfma(1);
-        interleave_phase<NM, P2, ND0>();
+        interleave_phase<NM, P2, ND0, NA>();
       }
     }
     wait_vmcnt<0>();
@@ -832,7 +844,7 @@ struct Plan {
 // Tile plan, from measurements on MI355X under sustained load.  The device
 // holds a lower clock under this GEMM than under MFMAs alone (feeding them
 // costs power), so the largest tile (256x256: fewest L2->LDS bytes per
-// operation, its main loop 91 % MFMA-busy against 86 % for 256x192) wins
+// operation, its main loop 87-91 % MFMA-busy against 85-86 % for 256x192) wins
 // once it fills several whole rounds of the CUs;
 // otherwise 256x192 when it fills at least three quarters of a round, and
 // 128x128 for small problems (more CUs busy).  With a short K (fewer than 16
