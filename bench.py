@@ -937,6 +937,11 @@ def main():
     if not args.no_extras:
         log("extras: MFMA-only loop for context")
         out["mfma_loop"] = mfma_loop(torch, timer)
+        if "tops" in out["mfma_loop"]:
+            # the int8 rate the device sustains with no data to move, beside
+            # the GEMM's (peak and frac stay priced at the published 5.0 POP/s)
+            out["roofline"]["mfma_loop_tops"] = out["mfma_loop"]["tops"]
+            out["roofline"]["frac_of_mfma_loop"] = round(gemm_tops / out["mfma_loop"]["tops"], 4)
         log("extras: vendor int8 GEMM for context")
         try:
             out["vendor_int_mm"] = vendor_int_mm(torch, cr, wl, timer)
