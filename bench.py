@@ -574,16 +574,17 @@ def _mfma_probe(torch):
     if not os.path.exists(path):
         return None
     lib = ctypes.CDLL(path)
-    lib.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.mfma_rate_launch.restype = ctypes.c_int
+    for fn in (lib.mfma_rate_launch, lib.mfma_rate_launch_bf16):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
     blocks = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
 
-    def run(iters):
-        rc = lib.mfma_rate_launch(blocks, iters, ctypes.c_void_p(out.data_ptr()),
-                                  ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    def run(iters, bf16=False):
+        fn = lib.mfma_rate_launch_bf16 if bf16 else lib.mfma_rate_launch
+        rc = fn(blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
         if rc:
-            raise RuntimeError(f"mfma_rate_launch failed: {rc}")
+            raise RuntimeError(f"mfma rate launch failed: {rc}")
     return run, out, blocks
 
 
@@ -604,9 +605,16 @@ def mfma_loop(torch, timer):
     consistent = bool(torch.equal(out, s1 * 2))
     t = timer.time(lambda i: run(MFMA_LOOP_ITERS), 5, warm=1)
     ops = blocks * 4 * MFMA_LOOP_ITERS * 8 * 65536
-    return {"workload": f"{blocks} workgroups x 4 waves x {MFMA_LOOP_ITERS} x 8 v_mfma_i32_32x32x32_i8",
-            "us": round(t * 1e6, 1), "tops": round(ops / t / 1e12, 1),
-            "frac": round(ops / t / 1e12 / PEAK_INT8_TOPS, 4), "work_doubles_with_iters": consistent}
+    res = {"workload": f"{blocks} workgroups x 4 waves x {MFMA_LOOP_ITERS} x 8 v_mfma_i32_32x32x32_i8",
+           "us": round(t * 1e6, 1), "tops": round(ops / t / 1e12, 1),
+           "frac": round(ops / t / 1e12 / PEAK_INT8_TOPS, 4), "work_doubles_with_iters": consistent}
+    # the same loop on v_mfma_f32_32x32x16_bf16 (32768 flops each), for the
+    # weight-only path's bf16 matmul
+    t16 = timer.time(lambda i: run(MFMA_LOOP_ITERS, bf16=True), 5, warm=1)
+    flops = blocks * 4 * MFMA_LOOP_ITERS * 8 * 32768
+    res["bf16"] = {"us": round(t16 * 1e6, 1), "tflops": round(flops / t16 / 1e12, 1),
+                   "frac": round(flops / t16 / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def device_info(torch):
@@ -955,6 +963,9 @@ def main():
         out["w4a8"] = extras_w4a8(torch, cr, wl, timer)
         log("extras: weight-only path M=2048 K=4096 N=12288")
         out["dequant_path"] = extras_dequant(torch, cr, wl, timer)
+        if "bf16" in out.get("mfma_loop", {}):
+            g = out["dequant_path"]["gemm_bf16"]
+            g["frac_of_mfma_loop"] = round(g["tflops"] / out["mfma_loop"]["bf16"]["tflops"], 4)
         log("extras: vision block, group 16")
         out["vision_g16"] = extras_vision(torch, cr, wl, timer)
         log("extras: 32-layer stack M=8704")

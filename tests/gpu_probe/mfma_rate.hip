@@ -1,6 +1,7 @@
-// Measurement helper (not part of the library): the int8 MFMA rate and the
-// shader clock the device holds when waves do nothing but
-// v_mfma_i32_32x32x32_i8, with no memory traffic.  Set beside the GEMM's
+// Measurement helper (not part of the library): the int8 (and bf16) MFMA
+// rate and the shader clock the device holds when waves do nothing but
+// v_mfma_i32_32x32x32_i8 (or v_mfma_f32_32x32x16_bf16), with no memory
+// traffic.  Set beside the GEMM's
 // counters it separates the cost of the matrix instructions themselves from
 // the cost of feeding them.
 //
@@ -59,11 +60,55 @@ __global__ __launch_bounds__(256, 2) void mfma_i8_loop(int iters, int* __restric
   out[t] = s;
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// The same loop on v_mfma_f32_32x32x16_bf16 (32768 flops each), for the
+// bf16 matmul of the weight-only path.  Fragments hold bf16 values in
+// [1, 2) (pseudo-random mantissas), so sums stay finite for any iters; each
+// lane writes the int32 bits of its float sum.
+__device__ __forceinline__ v4i frag_bf16(uint32_t seed) {
+  v4i f;
+  for (int i = 0; i < 4; ++i) f[i] = int((mix(seed * 4u + uint32_t(i)) & 0x007f007fu) | 0x3f803f80u);
+  return f;
+}
+
+__global__ __launch_bounds__(256, 2) void mfma_bf16_loop(int iters, int* __restrict__ out) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  const v8bf a0 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 0)), a1 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 1));
+  const v8bf a2 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 2)), a3 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 3));
+  const v8bf b0 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 4)), b1 = __builtin_bit_cast(v8bf, frag_bf16(t * 8u + 5));
+  v16f acc[8];
+  for (int j = 0; j < 8; ++j)
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  for (int i = 0; i < iters; ++i) {
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, acc[1], 0, 0, 0);
+    acc[2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b0, acc[2], 0, 0, 0);
+    acc[3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b1, acc[3], 0, 0, 0);
+    acc[4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, acc[4], 0, 0, 0);
+    acc[5] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, acc[5], 0, 0, 0);
+    acc[6] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, b1, acc[6], 0, 0, 0);
+    acc[7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, b0, acc[7], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 8; ++j)
+    for (int e = 0; e < 16; ++e) s += acc[j][e];
+  out[t] = __float_as_int(s);
+}
+
 }  // namespace
 
 // blocks workgroups of 256 threads; out holds blocks * 256 int32.
 extern "C" int mfma_rate_launch(int blocks, int iters, int* out, hipStream_t stream) {
   if (blocks <= 0 || iters < 0 || iters >= (1 << 20) || out == nullptr) return 1;
   hipLaunchKernelGGL(mfma_i8_loop, dim3(unsigned(blocks)), dim3(256), 0, stream, iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : 6;
+}
+
+// The bf16 loop; out holds blocks * 256 int32 (float bits).
+extern "C" int mfma_rate_launch_bf16(int blocks, int iters, int* out, hipStream_t stream) {
+  if (blocks <= 0 || iters < 0 || iters >= (1 << 20) || out == nullptr) return 1;
+  hipLaunchKernelGGL(mfma_bf16_loop, dim3(unsigned(blocks)), dim3(256), 0, stream, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }

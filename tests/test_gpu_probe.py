@@ -14,8 +14,9 @@ def _lib():
     if not os.path.exists(LIB):
         pytest.skip("tests/gpu_probe/libmfma_rate.so not built (run __graft_entry__.build())")
     lib = ctypes.CDLL(LIB)
-    lib.mfma_rate_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.mfma_rate_launch.restype = ctypes.c_int
+    for fn in (lib.mfma_rate_launch, lib.mfma_rate_launch_bf16):
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        fn.restype = ctypes.c_int
     return lib
 
 
@@ -25,6 +26,8 @@ def test_probe_exports_launcher_and_rejects_bad_arguments():
     assert lib.mfma_rate_launch(2, -1, ctypes.c_void_p(0x1000), None) == 1
     assert lib.mfma_rate_launch(2, 1 << 20, ctypes.c_void_p(0x1000), None) == 1
     assert lib.mfma_rate_launch(2, 1, None, None) == 1
+    assert lib.mfma_rate_launch_bf16(0, 1, ctypes.c_void_p(0x1000), None) == 1
+    assert lib.mfma_rate_launch_bf16(2, 1, None, None) == 1
 
 
 @pytest.mark.gpu
@@ -43,3 +46,24 @@ def test_probe_work_scales_with_iterations():
     assert torch.count_nonzero(sums[0]) == 0
     assert torch.count_nonzero(sums[1]) > 0
     assert torch.equal(sums[2], sums[1] * 2) and torch.equal(sums[3], sums[1] * 3)
+
+
+@pytest.mark.gpu
+def test_probe_bf16_loop_accumulates():
+    """The bf16 loop's sums (fp32 accumulation of bf16 products in [1, 4))
+    are finite, positive and grow with the iterations (the accumulation
+    order inside an MFMA is the hardware's, so the doubling is checked to
+    fp32 rounding, not exactly)."""
+    import torch
+    lib = _lib()
+    blocks = 8
+    out = torch.zeros((blocks * 256,), dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sums = []
+    for iters in (1, 2):
+        print(f"mfma probe bf16: {blocks} workgroups, {iters} iterations", flush=True)
+        assert lib.mfma_rate_launch_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), stream) == 0
+        torch.cuda.synchronize()
+        sums.append(out.view(torch.float32).double().clone())
+    assert torch.isfinite(sums[1]).all() and (sums[0] > 0).all()
+    assert torch.allclose(sums[1], 2 * sums[0], rtol=1e-5)
