@@ -94,6 +94,24 @@ def load_traffic(name, sources):
     return rec.get("traffic_bytes_per_launch")
 
 
+def load_mfma_busy():
+    """MFMA busy per SIMD over the engine cycles for the headline GEMM
+    (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs over SQ_CYCLES / 32 engines),
+    from the committed rocprofv3 counter summary of every tile plan, or None
+    when the GEMM source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "gemm_i8_tiles_lds_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(GEMM_SOURCES):
+        return None
+    for r in rec.get("records", []):
+        if (r["M"], r["N"], r["K"], r["weight_bits"]) == (M, N, K, 8):
+            return round(r["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (r["SQ_CYCLES"] / 32), 4)
+    return None
+
+
 class Timer:
     """Average duration of repeated launches, from HIP events recorded on the
     current stream (the one the library launches on)."""
@@ -919,6 +937,7 @@ def main():
             "unit": "TOPS",
             "frac": round(gemm_tops / PEAK_INT8_TOPS, 4),
             "traffic": load_traffic("gemm_i8_C3u", GEMM_SOURCES),
+            "mfma_busy_counter": load_mfma_busy(),
             "avg_launch_us": round(t_gemm * 1e6, 3),
             "algorithmic_ops_per_launch": ops,
         },
