@@ -686,14 +686,17 @@ def copy_peak(torch, timer):
             "elementwise": round(2 * (1 << 30) / t_ew / 1e9, 1)}
 
 
-# GEMM shapes whose tile plans the counter runs cover (M, N, K, weight bits):
-# the headline shape (256x192 tiles), the MLP down shape (256x128, three
-# stages), the attention shape M=512 (64x128, four stages) and M=4096,
-# N=12288 (256x256), int8 and int4 weights; each plan also at a second K, so
-# that counts which grow with K (the main loop) separate from those which do
-# not (set-up and epilogue).
-GEMM_TILE_SHAPES = [(2048, 12288, 4096, 8), (2048, 12288, 8192, 8), (2048, 4096, 12288, 8), (2048, 4096, 4096, 8),
-                    (512, 4096, 4096, 8), (512, 4096, 8192, 8), (4096, 12288, 4096, 8), (4096, 12288, 8192, 8),
+# GEMM shapes whose tile plans the counter runs cover (M, N, K, weight bits).
+# int8 weights: the headline shape (256x384, eight waves), M=2048, N=6144
+# (256x192), the MLP down shape (256x128, three stages), the attention shape
+# M=512 (64x128, four stages) and M=6144, N=12288 (256x256).  int4 weights:
+# M=2048, N=12288 (256x192), the MLP down shape, M=512 and M=4096, N=12288
+# (256x256).  Each plan also runs at a second K, so that counts which grow
+# with K (the main loop) separate from those which do not (set-up and
+# epilogue).
+GEMM_TILE_SHAPES = [(2048, 12288, 4096, 8), (2048, 12288, 8192, 8), (2048, 6144, 4096, 8), (2048, 6144, 8192, 8),
+                    (2048, 4096, 12288, 8), (2048, 4096, 4096, 8), (512, 4096, 4096, 8), (512, 4096, 8192, 8),
+                    (6144, 12288, 4096, 8), (6144, 12288, 8192, 8),
                     (2048, 12288, 4096, 4), (2048, 12288, 8192, 4), (2048, 4096, 12288, 4), (2048, 4096, 4096, 4),
                     (512, 4096, 4096, 4), (512, 4096, 8192, 4), (4096, 12288, 4096, 4), (4096, 12288, 8192, 4)]
 
@@ -931,7 +934,7 @@ def main():
                          "max_tops": round(ops / (reps[0] * 1e-3) / 1e12, 2)},
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_i8_k128_kernel (int8 MFMA GEMM + bf16 epilogue)",
+            "kernel": "gemm_i8_w8_kernel (eight-wave 256x384 int8 MFMA GEMM + bf16 epilogue)",
             "achieved": round(gemm_tops, 2),
             "peak": PEAK_INT8_TOPS,
             "unit": "TOPS",

@@ -30,6 +30,10 @@ SHAPES = [
     (4, 3069, 10752, 1344),   # 128x128, packed int4
     (4, 5384, 1407, 512),     # 128x128, packed int4
     (8, 1357, 5632, 448),     # 128x128
+    (8, 2048, 12288, 4096),   # 256x384, eight waves: one round
+    (8, 1920, 12288, 2048),   # 256x384, eight waves: one round, ragged M
+    (8, 4000, 12288, 4096),   # 256x384, eight waves: two rounds, ragged M
+    (8, 1024, 24576, 2048),   # 256x384, eight waves
 ]
 GUARD = 64  # elements before and after each output
 
@@ -66,3 +70,26 @@ def test_gemm_irregular_shapes(lib, wbits, M, N, K):
     assert np.array_equal(got, ref)
     yref = oracle.epilogue(ref.astype(np.int32), xs[rows], ws)
     assert np.array_equal(yh[GUARD:GUARD + M * N].reshape(M, N)[rows].view(np.uint16), yref)
+
+
+@pytest.mark.parametrize("M,N,K", [(1920, 12288, 2048), (2048, 12288, 4096)])
+def test_gemm_eight_wave_single_outputs(lib, M, N, K):
+    """The eight-wave 256x384 plan asked for the int32 accumulators alone and
+    for the bf16 output alone: each equal to the same launch with both."""
+    import torch
+    say(f"gemm_i8 eight-wave single outputs M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    a = to_dev(rng.integers(-127, 128, (M, K), dtype=np.int8))
+    b = to_dev(rng.integers(-127, 128, (N, K), dtype=np.int8))
+    xs = to_dev((rng.random(M) * 0.1 + 1e-3).astype(np.float32))
+    ws = to_dev((rng.random(N) * 1e-3 + 1e-5).astype(np.float32))
+    acc_both = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    y_both = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    acc_only = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+    y_only = torch.full((M, N), 7, dtype=torch.int16, device="cuda")
+    assert lib.convrot_gemm_i8(a, xs, b, 8, ws, M, N, K, acc_both, y_both) == 0
+    assert lib.convrot_gemm_i8(a, xs, b, 8, ws, M, N, K, acc_only, None) == 0
+    assert lib.convrot_gemm_i8(a, xs, b, 8, ws, M, N, K, None, y_only) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(acc_only, acc_both)
+    assert torch.equal(y_only, y_both)

@@ -738,6 +738,251 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
   gemm_k128_body<BM, BN, false, EVEN, false, true, NS>(X, nullptr, M, K, tiles_m, tiles_n, outs);
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave 256x384 tiles: int8 weights, one output, K a multiple of 256,
+// N a multiple of 384.  Two groups of four waves share the 256-token tile;
+// group g owns weight rows [192 g, 192 g + 192), and inside a group the
+// waves form the 2 x 2 grid of 128x96 blocks used above.  Per MFMA this
+// asks a third fewer lines of L2 than 256x192 (the main loop's cost follows
+// the lines its loads request).  The two 80 KB stages take all of LDS.
+//
+// With two waves per SIMD each wave reads one K-slice's fragments at a time
+// (one register set: 192 accumulators leave no room for a second), and the
+// other wave's MFMAs cover the LDS latency.  One barrier per 128-K step: the
+// loads of stage kt + 1 go out at the start of step kt into the buffer the
+// previous barrier freed, and are waited for at its end.  The last step is
+// peeled: instead of a stage it loads the tile's scales into the buffer it
+// does not read, where the epilogue finds them.  One workgroup per tile;
+// the plan is chosen where such tiles fill whole rounds of the CUs.
+constexpr int kW8Threads = 512;
+constexpr int kW8BM = 256, kW8BN = 384;
+constexpr int kW8GroupM = 8;  // M-tiles per block of the tile order
+
+__device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const float* __restrict__ sx, int M,
+                                             int K, int tiles_m, int tiles_n, const GemmOut& out) {
+  constexpr int BM = kW8BM, BN = kW8BN;
+  constexpr int W_BYTES = BN * 128, X_BYTES = BM * 128;  // one 128-K stage
+  constexpr int WL = W_BYTES / 1024 / 8, XL = X_BYTES / 1024 / 8;  // 1 KB loads per wave and stage
+  constexpr int TI = 3, TJ = 4;                                   // 128 tokens x 96 weight rows per wave
+  __shared__ __attribute__((aligned(1024))) int8_t sW0[W_BYTES], sW1[W_BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sX0[X_BYTES], sX1[X_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wm = (wave >> 1) & 1, wn = wave & 1;
+  const int row = lane & 31, half = lane >> 5;
+
+  // Tile: the XCD-aware order of the kernel above, in blocks of kW8GroupM
+  // M-tiles (a round of 32 tiles per XCD then spans 8 token tiles and 4
+  // weight tiles).
+  int tm, tn;
+  {
+    const int T = tiles_m * tiles_n, v = blockIdx.x;
+    const int t = (T & 7) == 0 ? (v & 7) * (T >> 3) + (v >> 3) : v;
+    const int nb = tiles_m / kW8GroupM, per_block = kW8GroupM * tiles_n, b = t / per_block;
+    if (b < nb) {
+      const int w = t - b * per_block;
+      tm = b * kW8GroupM + w % kW8GroupM;
+      tn = w / kW8GroupM;
+    } else {
+      const int h = tiles_m - nb * kW8GroupM, w = t - nb * per_block;
+      tm = nb * kW8GroupM + w % h;
+      tn = w / h;
+    }
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_x = min(BM, M - m0);  // N is a multiple of BN: weight tiles are whole
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X + int64_t(m0) * K),
+                                                                       short(0), rows_x * K, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(out.W + int64_t(n0) * K), short(0), BN * K, kBufFlags);
+
+  // Load block b (1 KB: rows 8b..8b+7, lane i writing LDS byte 16 i, which
+  // holds the chunk the row's swizzle puts there).  The swizzle of row r
+  // depends on bits 1..3 of r, so the lane offset of block b is that of
+  // block b & 1 plus (b >> 1) * 16 rows, which rides in the scalar offset.
+  unsigned off[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = 8 * p + (lane >> 3);
+    off[p] = unsigned(r * K + 16 * ((lane & 7) ^ swz128(r)));
+  }
+  auto issue = [&](int s, int k0) {
+    int8_t* const sX = s ? sX1 : sX0;
+    int8_t* const sW = s ? sW1 : sW0;
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+      const int b = wave * XL + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsx, (lds_ptr_t)(sX + b * 1024), 16, off[b & 1],
+                                               (b >> 1) * 16 * K + k0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < WL; ++j) {
+      const int b = wave * WL + j;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_ptr_t)(sW + b * 1024), 16, off[b & 1],
+                                               (b >> 1) * 16 * K + k0, 0, 0);
+    }
+  };
+  // Weight scales (384 floats, waves 0 and 1) at byte 0 of sW0 and token
+  // scales (256 floats, wave 2; rows past M read as zero) at byte 2048.
+  auto load_scales = [&]() {
+    if (wave < 3) {
+      const float* src = wave < 2 ? out.sw + n0 + 256 * wave : sx + m0;
+      const int nrec = wave == 0 ? 1024 : (wave == 1 ? 4 * (BN - 256) : 4 * rows_x);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
+                                                                          kBufFlags);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(sW0 + 1024 * wave), 16, unsigned(lane * 16), 0, 0,
+                                               0);
+    }
+  };
+
+  int wadr[TI], xadr[TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int r = grp * (BN / 2) + wn * 96 + i * 32 + row;
+    wadr[i] = r * 128 + 16 * (half ^ swz128(r));
+  }
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int r = wm * 128 + j * 32 + row;
+    xadr[j] = r * 128 + 16 * (half ^ swz128(r));
+  }
+  v4i fa[TI], fb[TJ];
+  v16i acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
+
+  // Step kt: multiply stage kt (buffer kt & 1, K-slice by K-slice) while
+  // stage kt + 1 (or, on the last step, the scales) lands in the other.
+  auto step = [&](int kt, auto last_c) {
+    constexpr bool LAST = decltype(last_c)::value;
+    const int s = kt & 1;
+    const int8_t* const bw = s ? sW1 : sW0;
+    const int8_t* const bx = s ? sX1 : sX0;
+    if constexpr (LAST)
+      load_scales();
+    else
+      issue(s ^ 1, (kt + 1) * 128);
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) fa[i] = *reinterpret_cast<const v4i*>(bw + (wadr[i] ^ (32 * sl)));
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) fb[j] = *reinterpret_cast<const v4i*>(bx + (xadr[j] ^ (32 * sl)));
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // K / 128 steps, an even number: the last step reads buffer 1, so the
+  // scales go to buffer 0.
+  const int ksteps = K / 128;
+  issue(0, 0);
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  for (int kt = 0; kt < ksteps - 1; ++kt) step(kt, std::false_type{});
+  step(ksteps - 1, std::true_type{});
+
+  // Epilogue (as above): scales from sW0, each wave's 32-token blocks staged
+  // in buffer 1 (waves 0-5 in sW1, 6-7 in sX1) for 16-byte row stores.
+  const float* const sSw = reinterpret_cast<const float*>(sW0);
+  const float* const sSx = reinterpret_cast<const float*>(sW0 + 2048);
+  const int N = out.N, ldy = out.ldy;
+  const int wrow0 = n0 + grp * (BN / 2) + wn * 96;  // this wave's first weight row
+  if (out.acc) {
+    const bool vec_ok = ((N | ldy) & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int m = m0 + wm * 128 + j * 32 + row;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = wrow0 + i * 32 + 8 * g + 4 * half;
+          int32_t* const dst = out.acc + int64_t(m) * ldy + n;
+          if (vec_ok) {
+            *reinterpret_cast<int4*>(dst) =
+                make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = acc[i][j][4 * g + e];
+          }
+        }
+    }
+  }
+  if (out.y) {
+    constexpr int NQ = 12, P = 208, STG = 7 * 1024;  // 96 bf16 per row: 12 chunks, padded rows
+    static_assert(6 * STG <= W_BYTES && 2 * STG <= X_BYTES, "staging blocks");
+    int8_t* const stage_buf = wave < 6 ? sW1 + wave * STG : sX1 + (wave - 6) * STG;
+    const bool interior = m0 + BM <= M && ((N | ldy) & 7) == 0;
+    float4 sw4s[TI][4];
+    float sxv[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + (wrow0 - n0) + 4 * half + i * 32 + 8 * g);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * 128 + j * 32 + row];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 sw4 = sw4s[i][g];
+          const float f0 = (float(acc[i][j][4 * g + 0]) * sxv[j]) * sw4.x;
+          const float f1 = (float(acc[i][j][4 * g + 1]) * sxv[j]) * sw4.y;
+          const float f2 = (float(acc[i][j][4 * g + 2]) * sxv[j]) * sw4.z;
+          const float f3 = (float(acc[i][j][4 * g + 3]) * sxv[j]) * sw4.w;
+          *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * (i * 4 + g) + 8 * half) =
+              make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
+        }
+#pragma unroll
+      for (int k = 0; k < 32 * NQ / 64; ++k) {
+        const int id = lane + 64 * k;
+        const int r = id / NQ, q = id % NQ;
+        const int m = m0 + wm * 128 + j * 32 + r;
+        const int n = wrow0 + 8 * q;
+        const uint4 v = *reinterpret_cast<const uint4*>(stage_buf + r * P + 16 * q);
+        if (interior) {
+          store_nt(out.y + int64_t(m) * ldy + n, v);
+        } else if (m < M) {
+          if (((N | ldy) & 7) == 0) {
+            store_nt(out.y + int64_t(m) * ldy + n, v);
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out.y[int64_t(m) * ldy + n + e] = uint16_t(w[e / 2] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kW8Threads, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ X,
+                                                                   const float* __restrict__ sx, int M, int K,
+                                                                   int tiles_m, int tiles_n, GemmOut out) {
+  gemm_w8_body(X, sx, M, K, tiles_m, tiles_n, out);
+}
+
 // Workgroups of kernel K the current device runs at once: compute units x
 // resident workgroups per unit, a multiple of 8 on MI355X (256 units, one or
 // two per unit), so the persistent tile order stays XCD-aware.  A read-only
@@ -802,6 +1047,21 @@ hipError_t launch_k128(const int8_t* xq, const float* x_scale, int M, int K, con
   return hipGetLastError();
 }
 
+// One launch of the eight-wave 256x384 kernel (int8 weights, one output,
+// K % 256 == 0, N % 384 == 0): one workgroup per tile.
+hipError_t launch_w8(const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc& d,
+                     hipStream_t stream) {
+  const GemmOut o{static_cast<const uint8_t*>(d.wq), d.w_scale, d.acc, d.y, d.N, d.ldy};
+  const int tiles_m = (M + kW8BM - 1) / kW8BM, tiles_n = d.N / kW8BN;
+  hipLaunchKernelGGL(gemm_i8_w8_kernel, dim3(unsigned(int64_t(tiles_m) * tiles_n)), dim3(kW8Threads), 0, stream,
+                     xq, x_scale, M, K, tiles_m, tiles_n, o);
+  return hipGetLastError();
+}
+
+bool w8_fits(int64_t K, const GemmOutDesc* d, int n) {
+  return n == 1 && K % 256 == 0 && d[0].N % kW8BN == 0;
+}
+
 struct TileChoice {
   int bm, bn;
   int ns = 2;  // pipeline stages
@@ -810,8 +1070,10 @@ struct TileChoice {
 // Tuning builds only (-DCONVROT_TUNING): CONVROT_GEMM_TILE=<BM>x<BN>[x<stages>]
 // forces one of the tile shapes above (the deeper pipelines: 256x128x3,
 // 128x256x3, 128x128x3, 128x128x4, 64x128x4, 128x64x4 for int8 and int4
-// weights, the first, fourth and fifth for bf16), for sweeps: every choice
-// gives bit-identical results.  The library as built reads no environment.
+// weights, the first, fourth and fifth for bf16; 256x384, the eight-wave
+// tiles, for int8 weights with N % 384 == 0 and K % 256 == 0), for sweeps:
+// every choice gives bit-identical results.  The library as built reads no
+// environment.
 TileChoice tile_override() {
 #ifdef CONVROT_TUNING
   static const TileChoice forced = [] {
@@ -899,6 +1161,19 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   return {128, 128};
 }
 
+// The eight-wave 256x384 plan (int8 weights, one output), where its tiles
+// make one or two whole rounds of the CUs and K has at least 16 stages:
+// M 2048, K 4096, N 12288 (256 tiles) 95.7 -> 87.2 us against 256x192,
+// K 8192 182.6 -> 167.8 us; M 4096 (two rounds) 176.2 -> 173.8 us against
+// 256x256 (same box, interleaved, bit-identical outputs).  It takes one tile
+// per workgroup, so a partial last round would leave CUs idle.
+bool w8_whole_rounds(int64_t M, int64_t K, const GemmOutDesc* d, int n) {
+  if (!w8_fits(K, d, n) || K / 128 < 16) return false;
+  const int64_t cus = device_cus();
+  const int64_t tiles = ((M + kW8BM - 1) / kW8BM) * (d[0].N / kW8BN);
+  return tiles % cus == 0 && tiles <= 2 * cus;
+}
+
 // Tuning builds only (-DCONVROT_TUNING):
 // CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan for a single
 // output, for sweeps (every plan gives bit-identical results).
@@ -925,6 +1200,11 @@ bool plan_override(Plan& out) {
 template <bool W4>
 hipError_t launch_tile(TileChoice tc, const int8_t* xq, const float* x_scale, int M, int K, const GemmOutDesc* d,
                        int n, hipStream_t stream) {
+  // Eight-wave 256x384 tiles (int8 weights; others take 256x192).
+  if (tc.bm == 256 && tc.bn == 384) {
+    if (!W4 && w8_fits(K, d, n)) return launch_w8(xq, x_scale, M, K, d[0], stream);
+    tc = {256, 192};
+  }
   // Deeper pipelines (one tile per workgroup).
   if (tc.ns == 3 && tc.bm == 256 && tc.bn == 128) return launch_k128<256, 128, W4, 3>(xq, x_scale, M, K, d, n, stream);
   if (tc.ns == 3 && tc.bm == 128 && tc.bn == 256) return launch_k128<128, 256, W4, 3>(xq, x_scale, M, K, d, n, stream);
@@ -960,6 +1240,7 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     return hipSuccess;
   }
   const TileChoice forced = tile_override();
+  if (!W4 && !forced.bm && w8_whole_rounds(M, K, d, n)) return launch_w8(xq, x_scale, M, K, d[0], stream);
   const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
   return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
