@@ -739,8 +739,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
 }
 
 // ---------------------------------------------------------------------------
-// Eight-wave 256x384 tiles: int8 weights, one output, K a multiple of 256,
-// N a multiple of 384.  Two groups of four waves share the 256-token tile;
+// Eight-wave 256x384 tiles: int8 weights with one output, or the bf16 matmul
+// of the weight-only path (BF: K counts row bytes, fp32 accumulators,
+// y = bf16(acc)); K a multiple of 256 bytes, N a multiple of 384.  Two groups of four waves share the 256-token tile;
 // group g owns weight rows [192 g, 192 g + 192), and inside a group the
 // waves form the 2 x 2 grid of 128x96 blocks used above.  Per MFMA this
 // asks a third fewer lines of L2 than 256x192 (the main loop's cost follows
@@ -751,13 +752,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
 // other wave's MFMAs cover the LDS latency.  One barrier per 128-K step: the
 // loads of stage kt + 1 go out at the start of step kt into the buffer the
 // previous barrier freed, and are waited for at its end.  The last step is
-// peeled: instead of a stage it loads the tile's scales into the buffer it
-// does not read, where the epilogue finds them.  One workgroup per tile;
+// peeled: instead of a stage it loads the tile's scales (int8 only) into
+// the buffer it does not read, where the epilogue finds them.  One workgroup per tile;
 // the plan is chosen where such tiles fill whole rounds of the CUs.
 constexpr int kW8Threads = 512;
 constexpr int kW8BM = 256, kW8BN = 384;
 constexpr int kW8GroupM = 8;  // M-tiles per block of the tile order
 
+template <bool BF>
 __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const float* __restrict__ sx, int M,
                                              int K, int tiles_m, int tiles_n, const GemmOut& out) {
   constexpr int BM = kW8BM, BN = kW8BN;
@@ -849,7 +851,8 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
     xadr[j] = r * 128 + 16 * (half ^ swz128(r));
   }
   v4i fa[TI], fb[TJ];
-  v16i acc[TI][TJ];
+  using AccT = std::conditional_t<BF, v16f, v16i>;
+  AccT acc[TI][TJ];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
 #pragma unroll
@@ -864,10 +867,11 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
     const int s = kt & 1;
     const int8_t* const bw = s ? sW1 : sW0;
     const int8_t* const bx = s ? sX1 : sX0;
-    if constexpr (LAST)
-      load_scales();
-    else
+    if constexpr (LAST) {
+      if constexpr (!BF) load_scales();
+    } else {
       issue(s ^ 1, (kt + 1) * 128);
+    }
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
 #pragma unroll
@@ -878,7 +882,11 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int j = 0; j < TJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          if constexpr (BF)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, fa[i]),
+                                                                __builtin_bit_cast(v8bf, fb[j]), acc[i][j], 0, 0, 0);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     wait_vmcnt<0>();
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
@@ -904,7 +912,7 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
   const float* const sSx = reinterpret_cast<const float*>(sW0 + 2048);
   const int N = out.N, ldy = out.ldy;
   const int wrow0 = n0 + grp * (BN / 2) + wn * 96;  // this wave's first weight row
-  if (out.acc) {
+  if (!BF && out.acc) {
     const bool vec_ok = ((N | ldy) & 3) == 0;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
@@ -917,11 +925,11 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
           const int n = wrow0 + i * 32 + 8 * g + 4 * half;
           int32_t* const dst = out.acc + int64_t(m) * ldy + n;
           if (vec_ok) {
-            *reinterpret_cast<int4*>(dst) =
-                make_int4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            *reinterpret_cast<int4*>(dst) = make_int4(int(acc[i][j][4 * g]), int(acc[i][j][4 * g + 1]),
+                                                      int(acc[i][j][4 * g + 2]), int(acc[i][j][4 * g + 3]));
           } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[e] = acc[i][j][4 * g + e];
+            for (int e = 0; e < 4; ++e) dst[e] = int(acc[i][j][4 * g + e]);
           }
         }
     }
@@ -931,26 +939,36 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
     static_assert(6 * STG <= W_BYTES && 2 * STG <= X_BYTES, "staging blocks");
     int8_t* const stage_buf = wave < 6 ? sW1 + wave * STG : sX1 + (wave - 6) * STG;
     const bool interior = m0 + BM <= M && ((N | ldy) & 7) == 0;
-    float4 sw4s[TI][4];
+    float4 sw4s[TI][4];  // (the bf16 product has no scales)
     float sxv[TJ];
+    if constexpr (!BF) {
 #pragma unroll
-    for (int i = 0; i < TI; ++i)
+      for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + (wrow0 - n0) + 4 * half + i * 32 + 8 * g);
+        for (int g = 0; g < 4; ++g)
+          sw4s[i][g] = *reinterpret_cast<const float4*>(sSw + (wrow0 - n0) + 4 * half + i * 32 + 8 * g);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * 128 + j * 32 + row];
+      for (int j = 0; j < TJ; ++j) sxv[j] = sSx[wm * 128 + j * 32 + row];
+    }
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
 #pragma unroll
       for (int i = 0; i < TI; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 sw4 = sw4s[i][g];
-          const float f0 = (float(acc[i][j][4 * g + 0]) * sxv[j]) * sw4.x;
-          const float f1 = (float(acc[i][j][4 * g + 1]) * sxv[j]) * sw4.y;
-          const float f2 = (float(acc[i][j][4 * g + 2]) * sxv[j]) * sw4.z;
-          const float f3 = (float(acc[i][j][4 * g + 3]) * sxv[j]) * sw4.w;
+          float f0, f1, f2, f3;
+          if constexpr (BF) {
+            f0 = acc[i][j][4 * g + 0];
+            f1 = acc[i][j][4 * g + 1];
+            f2 = acc[i][j][4 * g + 2];
+            f3 = acc[i][j][4 * g + 3];
+          } else {
+            const float4 sw4 = sw4s[i][g];
+            f0 = (float(acc[i][j][4 * g + 0]) * sxv[j]) * sw4.x;
+            f1 = (float(acc[i][j][4 * g + 1]) * sxv[j]) * sw4.y;
+            f2 = (float(acc[i][j][4 * g + 2]) * sxv[j]) * sw4.z;
+            f3 = (float(acc[i][j][4 * g + 3]) * sxv[j]) * sw4.w;
+          }
           *reinterpret_cast<uint2*>(stage_buf + row * P + 16 * (i * 4 + g) + 8 * half) =
               make_uint2(pack_bf16x2(f0, f1), pack_bf16x2(f2, f3));
         }
@@ -980,7 +998,13 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
 __global__ __launch_bounds__(kW8Threads, 1) void gemm_i8_w8_kernel(const int8_t* __restrict__ X,
                                                                    const float* __restrict__ sx, int M, int K,
                                                                    int tiles_m, int tiles_n, GemmOut out) {
-  gemm_w8_body(X, sx, M, K, tiles_m, tiles_n, out);
+  gemm_w8_body<false>(X, sx, M, K, tiles_m, tiles_n, out);
+}
+
+// The bf16 matmul on the same tiles (K counts row bytes).
+__global__ __launch_bounds__(kW8Threads, 1) void gemm_bf16_w8_kernel(const int8_t* __restrict__ X, int M, int K,
+                                                                     int tiles_m, int tiles_n, GemmOut out) {
+  gemm_w8_body<true>(X, nullptr, M, K, tiles_m, tiles_n, out);
 }
 
 // Workgroups of kernel K the current device runs at once: compute units x
@@ -1167,11 +1191,11 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
 // K 8192 182.6 -> 167.8 us; M 4096 (two rounds) 176.2 -> 173.8 us against
 // 256x256 (same box, interleaved, bit-identical outputs).  It takes one tile
 // per workgroup, so a partial last round would leave CUs idle.
-bool w8_whole_rounds(int64_t M, int64_t K, const GemmOutDesc* d, int n) {
+bool w8_whole_rounds(int64_t M, int64_t K, const GemmOutDesc* d, int n, int max_rounds = 2) {
   if (!w8_fits(K, d, n) || K / 128 < 16) return false;
   const int64_t cus = device_cus();
   const int64_t tiles = ((M + kW8BM - 1) / kW8BM) * (d[0].N / kW8BN);
-  return tiles % cus == 0 && tiles <= 2 * cus;
+  return tiles % cus == 0 && tiles <= max_rounds * cus;
 }
 
 // Tuning builds only (-DCONVROT_TUNING):
@@ -1276,6 +1300,17 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t stream) {
   const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
   const TileChoice forced = tile_override();
+  // Eight-wave 256x384 tiles where they make exactly one round (K in
+  // bytes): M 2048, K 4096, N 12288 174.8 -> 161.2 us (same box,
+  // interleaved, identical outputs); at two rounds (M 4096) 256x256 stays
+  // ahead, 309.8 against 312.0 us.
+  if (!forced.bm && w8_whole_rounds(M, 2 * K, &d, 1, 1)) {
+    const GemmOut o{reinterpret_cast<const uint8_t*>(w), nullptr, nullptr, y, int(N), int(N)};
+    const int tiles_m = int((M + kW8BM - 1) / kW8BM), tiles_n = int(N / kW8BN);
+    hipLaunchKernelGGL(gemm_bf16_w8_kernel, dim3(unsigned(int64_t(tiles_m) * tiles_n)), dim3(kW8Threads), 0, stream,
+                       reinterpret_cast<const int8_t*>(x), int(M), int(2 * K), tiles_m, tiles_n, o);
+    return hipGetLastError();
+  }
   const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1);
   if (tc.ns == 3 && tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128, 3>(x, w, int(M), int(N), int(K), y, stream);
   if (tc.ns == 4 && tc.bm == 128 && tc.bn == 128) return launch_bf16<128, 128, 4>(x, w, int(M), int(N), int(K), y, stream);
