@@ -741,11 +741,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
 // ---------------------------------------------------------------------------
 // Eight-wave 256x384 tiles: int8 weights with one output, or the bf16 matmul
 // of the weight-only path (BF: K counts row bytes, fp32 accumulators,
-// y = bf16(acc)); K a multiple of 256 bytes, N a multiple of 384.  Two groups of four waves share the 256-token tile;
-// group g owns weight rows [192 g, 192 g + 192), and inside a group the
-// waves form the 2 x 2 grid of 128x96 blocks used above.  Per MFMA this
-// asks a third fewer lines of L2 than 256x192 (the main loop's cost follows
-// the lines its loads request).  The two 80 KB stages take all of LDS.
+// y = bf16(acc)); K a multiple of 256 bytes, N a multiple of 384.  Two
+// groups of four waves share the 256-token tile; group g owns weight rows
+// [192 g, 192 g + 192), and inside a group the waves form the 2 x 2 grid of
+// 128x96 blocks used above.  Per MFMA this asks a third fewer lines of L2
+// than 256x192 (the main loop's cost follows the lines its loads request).
+// The two 80 KB stages take all of LDS.
 //
 // With two waves per SIMD each wave reads one K-slice's fragments at a time
 // (one register set: 192 accumulators leave no room for a second), and the
@@ -753,8 +754,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
 // loads of stage kt + 1 go out at the start of step kt into the buffer the
 // previous barrier freed, and are waited for at its end.  The last step is
 // peeled: instead of a stage it loads the tile's scales (int8 only) into
-// the buffer it does not read, where the epilogue finds them.  One workgroup per tile;
-// the plan is chosen where such tiles fill whole rounds of the CUs.
+// the buffer it does not read, where the epilogue finds them.  One
+// workgroup per tile; the plan is chosen where such tiles fill whole rounds
+// of the CUs.
 constexpr int kW8Threads = 512;
 constexpr int kW8BM = 256, kW8BN = 384;
 constexpr int kW8GroupM = 8;  // M-tiles per block of the tile order
