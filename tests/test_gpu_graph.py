@@ -13,7 +13,7 @@ from w8a8_quantized_linear_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-# Headline shape (persistent 256x192 tiles), a small one (64x128 tiles,
+# Headline shape (eight-wave 256x384 tiles), a small one (64x128 tiles,
 # four stages) and a long-K one (256x128 tiles, three stages).
 @pytest.mark.parametrize("M,K,N", [(2048, 4096, 12288), (512, 4096, 4096), (2048, 12288, 4096)])
 def test_w8a8_linear_graph_replays(lib, M, K, N):

@@ -34,7 +34,7 @@ def _weights(rng, Ns, K, wbits):
     (8, 33, 512, (512, 128, 128)),            # q/k/v-like, small M: 64x128 tiles, four stages
     (8, 130, 272, (70, 257, 33)),             # ragged N and K (tail kernel)
     (8, 300, 1024, (16,) * 8),                # eight tiny outputs
-    (8, 2048, 512, (4096, 1024, 1024)),       # 256x192 tiles across three outputs
+    (8, 2048, 512, (4096, 1024, 1024)),       # 128x128 tiles across three outputs (short K)
     (8, 2048, 256, (12288, 12288)),           # 256x256 tiles (every N a multiple of 256)
     (8, 2048, 2048, (2048, 1024, 1024)),      # 256x128 tiles, three stages, one per CU
     (4, 64, 1024, (512, 96, 1000)),           # packed int4

@@ -39,17 +39,17 @@ def test_gemm_i8_bit_exact(lib, M, N, K):
 
 
 @pytest.mark.parametrize("wbits,M,N,K", [
-    (8, 2048, 12288, 512),   # 256x192, persistent
-    (8, 8704, 4096, 256),    # 256x192, three tiles per workgroup
+    (8, 2048, 6144, 2048),   # 256x192, persistent
+    (8, 8704, 4096, 2048),   # 256x192, about three tiles per workgroup
     (8, 2048, 4096, 768),    # 128x128
     (8, 2048, 4096, 640),    # 128x128, K an odd number of 128-steps
     (8, 2048, 4096, 2048),   # 256x128 with three stages, one tile per CU
     (8, 1990, 4090, 2064),   # the same, ragged M, N and K
     (8, 512, 4000, 1040),    # 64x128 with four stages, ragged N and K
     (8, 1000, 4000, 1040),   # 128x128 with four stages, ragged M, N and K
-    (8, 2000, 12280, 512),   # 256x192, ragged M and N (N not a multiple of 8)
+    (8, 2000, 12280, 2048),  # 256x192, ragged M and N (N not a multiple of 8)
     (8, 8700, 12288, 256),   # 256x256, ragged M
-    (4, 2048, 12288, 512),   # packed int4, 256x192
+    (4, 2048, 12288, 2048),  # packed int4, 256x192
     (4, 4000, 12288, 256),   # packed int4, 256x256, ragged M
     (4, 1990, 4090, 2080),   # packed int4, 256x128 with three stages, ragged M, N and K
     (4, 1000, 4000, 1056),   # packed int4, 128x128 with four stages
@@ -422,8 +422,10 @@ def test_concurrent_host_threads(lib):
     import threading
     import torch
     say("gemm_i8 from two host threads on two streams")
-    # plans: 128x128 persistent, 256x192 persistent, range-checked K, 256x256
-    shapes = [(512, 4096, 512), (2048, 12288, 256), (300, 1000, 1040), (8704, 12288, 256)]
+    # plans: 64x128 four-stage, 128x128 persistent, range-checked K, 256x256,
+    # 256x192 persistent, eight-wave 256x384
+    shapes = [(512, 4096, 512), (2048, 12288, 256), (300, 1000, 1040), (8704, 12288, 256), (2048, 6144, 2048),
+              (2048, 12288, 2048)]
     errors = []
 
     def worker(idx):
