@@ -81,12 +81,12 @@ def test_gemm_bf16_full(lib, M, N, K):
     assert_gemm_bf16_close(y, oracle.gemm_bf16(x, w), x, w)
 
 
-@pytest.mark.parametrize("M,N,K", [(2048, 12288, 512), (8704, 4096, 256), (2000, 12280, 528), (4096, 12288, 256),
+@pytest.mark.parametrize("M,N,K", [(2048, 6144, 1024), (8704, 4096, 256), (2000, 12280, 1040), (4096, 12288, 256),
                                    (2048, 4096, 6144), (1990, 4090, 2064), (1000, 4000, 1040), (2048, 4096, 1088)])
 def test_gemm_bf16_large_sampled(lib, M, N, K):
-    """The large tile plans (persistent 256x192, 256x256, ragged edges) and
-    the deeper pipelines (256x128 three-stage, even and ragged; 128x128
-    four-stage) on sampled rows against the oracle."""
+    """The large tile plans (persistent 256x192, even and ragged; 256x256;
+    128x128 persistent) and the deeper pipelines (256x128 three-stage, even
+    and ragged; 128x128 four-stage) on sampled rows against the oracle."""
     say(f"gemm_bf16 large M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N + K + 1)
     x = wl.float_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
