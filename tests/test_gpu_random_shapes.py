@@ -35,7 +35,7 @@ SHAPES = [
     (8, 4000, 12288, 4096),   # 256x384, eight waves: two rounds, ragged M
     (8, 1024, 24576, 2048),   # 256x384, eight waves
     (4, 2048, 12288, 4096),   # 256x192, packed int4
-    (4, 3900, 12288, 2048),   # 256x192, packed int4, ragged M
+    (4, 3900, 12288, 2048),   # 256x256, packed int4, ragged M
 ]
 GUARD = 64  # elements before and after each output
 
