@@ -17,7 +17,7 @@ SHAPES = [
     (1, 256, 256, False), (3001, 2560, 256, False), (4095, 4352, 256, False), (4097, 4096, 256, False),
     (777, 12544, 256, False), (12, 16384, 256, False), (2049, 1152, 16, False), (333, 4304, 16, False),
     (5000, 8192, 16, False), (4099, 512, 1, False), (17, 8000, 1, False), (999, 3328, 256, True),
-    (4100, 6400, 256, True), (5, 16384, 256, True),
+    (4100, 6400, 256, True), (5, 16384, 256, True), (4103, 3328, 256, True),
 ]
 GUARD = 256
 

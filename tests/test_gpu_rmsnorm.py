@@ -122,3 +122,33 @@ def test_rmsnorm_stack_shape_sampled(lib):
     xq_ref, xs_ref, _ = oracle.rmsnorm_rotate_quant(x[toks], w, eps=1e-6)
     assert_scales_close(xs.cpu().numpy()[toks], xs_ref)
     assert_codes_close(xq.cpu().numpy()[toks], xq_ref)
+
+
+# (M, K): at least 4096 tokens with one wave per token (K up to 4096), the
+# shapes on which the call without the bf16 norm output walks the tokens
+# with a resident grid.  The token counts leave ragged last rounds, and the
+# larger ones make some workgroups take several rounds.
+WALK_CASES = [(4099, 4096), (8704, 4096), (4101, 3840), (8195, 3072), (9000, 2048), (8200, 1024),
+              (20001, 4096)]
+
+
+@pytest.mark.parametrize("M,K", WALK_CASES)
+def test_rmsnorm_token_walk(lib, M, K):
+    """Without the bf16 output the fused call walks the tokens; its codes and
+    scales must equal bit for bit those of the call that also writes the norm
+    output (one workgroup per four tokens), and match the oracle on sampled
+    tokens, the ragged tail included."""
+    say(f"rmsnorm_rotate_quant token walk M={M} K={K}")
+    x, w = _inputs(M, K, seed=M + 3 * K)
+    xd, wd = bf16_to_dev(x), to_dev(w)
+    xq, xs = lib.rmsnorm_rotate_quant(xd, wd, eps=1e-6)
+    xq2, xs2, _ = lib.rmsnorm_rotate_quant(xd, wd, eps=1e-6, want_y=True)
+    q, s = xq.cpu().numpy(), xs.cpu().numpy()
+    assert np.array_equal(q, xq2.cpu().numpy())
+    assert np.array_equal(s, xs2.cpu().numpy())
+    rng = np.random.default_rng(M)
+    toks = np.unique(np.concatenate([rng.choice(M, 64, replace=False), np.arange(M - 9, M), [0, 4095, 4096]]))
+    toks = toks[toks < M]
+    xq_ref, xs_ref, _ = oracle.rmsnorm_rotate_quant(x[toks], w, eps=1e-6)
+    assert_scales_close(s[toks], xs_ref)
+    assert_codes_close(q[toks], xq_ref)

@@ -35,6 +35,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 namespace convrot {
 namespace {
@@ -98,13 +99,24 @@ __device__ __forceinline__ void max3_abs(float& m, float a, float b) {
   asm("v_max3_f32 %0, |%1|, |%2|, %0" : "+v"(m) : "v"(a), "v"(b));
 }
 
-template <int C, int TW, bool NORM>
+// bf16 rounding (to nearest even) of v, as an fp32 value: one convert that
+// puts v's bf16 in the high half of the word and +0 in the low half.
+__device__ __forceinline__ float round_bf16(float v) { return __uint_as_float(pack_bf16x2(0.0f, v)); }
+
+// One token per TW waves.  WALK (TW = 1 only): a workgroup of the resident
+// grid walks the tokens, its wave w taking w + 4 * (blockIdx.x + i *
+// gridDim.x) for i = 0, 1, ..., so set-up (the RMSNorm factors in LDS) is
+// paid once per workgroup rather than once per four tokens.  The waves of a
+// workgroup then run their loops independently: nothing after the set-up
+// waits on a barrier.
+template <int C, int TW, bool NORM, bool WALK = false>
 __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                      int K, int8_t* __restrict__ xq,
                                                                      float* __restrict__ x_scale,
                                                                      const float* __restrict__ norm_w, float eps,
                                                                      uint16_t* __restrict__ y_norm) {
   static_assert(TW == 1 || TW == 2 || TW == 4, "waves per token");
+  static_assert(!WALK || TW == 1, "a walking wave holds whole tokens");
   constexpr int P = kWaves / TW;  // tokens per workgroup iteration
   __shared__ float red[kWaves];
   __shared__ double red_d[kWaves];
@@ -130,12 +142,11 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
   // and are neither loaded nor stored.  Uniform over a 16-lane group.
   const int nvalid = K >> 8;
   auto slot_ok = [&](int j) { return ((j * TW + wt) * 4 + (lane >> 4)) < nvalid; };
-
-  u32x4 raw[C][2];
   // Every slot in use (the common widths: 16, 32, 48 and 64 groups): plain
   // loads, with no zero fill to keep for the masked case.
   const bool full = nvalid == 4 * C * TW;  // uniform
-  auto load = [&](int64_t tok) {
+
+  auto load = [&](u32x4 (&raw)[C][2], int64_t tok) {
     if (tok < M) {
       const uint16_t* row = x + tok * K;
       if (full) {
@@ -196,29 +207,28 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       }
   }
 
-  {
-    const int64_t tok = int64_t(blockIdx.x) * P + wave / TW;
-    load(tok);
-    uint32_t wd[C][8];  // the row's bf16 pairs as loaded (or as normalised)
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wd[j][i] = raw[j][0][i];
-        wd[j][4 + i] = raw[j][1][i];
-      }
-
+  // Normalise (NORM), rotate and quantize the token held in raw.
+  auto process = [&](const u32x4 (&raw)[C][2], int64_t tok) {
+    float v[C][16];
     if constexpr (NORM) {
+      float f[C][16];  // the row as loaded
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w = raw[j][i >> 2][i & 3];
+          f[j][2 * i] = __uint_as_float(w << 16);
+          f[j][2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        }
       // mean square in fp64 (each square of a bf16 value is exact there),
       // then y = bf16_rne((x * r) * (1 + w)) with r = 1 / sqrt(ms + eps)
       double ss = 0.0;
 #pragma unroll
       for (int j = 0; j < C; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const double lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
-          ss = __builtin_fma(lo, lo, ss);
-          ss = __builtin_fma(hi, hi, ss);
+        for (int i = 0; i < 16; ++i) {
+          const double d = f[j][i];
+          ss = __builtin_fma(d, d, ss);
         }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
@@ -233,42 +243,54 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
       }
       const float ms = float(ss / double(K));
       const float r = 1.0f / sqrtf(ms + eps);
+      // An index the compiler cannot see through, so the walking kernel
+      // reads the factors from LDS for each token instead of holding all
+      // of them in registers across its loop (16 per chunk).
+      int wl = lane;
+      if constexpr (WALK) asm volatile("" : "+v"(wl));
+      const bool want_y = y_norm != nullptr && tok < M;
 #pragma unroll
       for (int j = 0; j < C; ++j) {
+        float y[16];  // the normalised values, rounded to bf16
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float w1[4];
           if constexpr (kW1Lds) {
-            const float4 f = w1s[((j * TW + wt) * 4 + q) * 64 + lane];
-            w1[0] = f.x, w1[1] = f.y, w1[2] = f.z, w1[3] = f.w;
+            const float4 wf = w1s[((j * TW + wt) * 4 + q) * 64 + wl];
+            w1[0] = wf.x, w1[1] = wf.y, w1[2] = wf.z, w1[3] = wf.w;
           } else {
 #pragma unroll
             for (int h = 0; h < 4; ++h) w1[h] = w1r[j][4 * q + h];
           }
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int i = 2 * q + h;
-            const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
-            wd[j][i] = pack_bf16x2((lo * r) * w1[2 * h], (hi * r) * w1[2 * h + 1]);
-          }
+          for (int h = 0; h < 4; ++h) y[4 * q + h] = round_bf16((f[j][4 * q + h] * r) * w1[h]);
         }
-        if (y_norm != nullptr && tok < M && slot_ok(j)) {
+        if (want_y && slot_ok(j)) {
+          uint32_t p[8];  // the high halves of consecutive pairs
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            p[i] = __builtin_amdgcn_perm(__float_as_uint(y[2 * i + 1]), __float_as_uint(y[2 * i]), 0x07060302u);
           u32x4* dst = reinterpret_cast<u32x4*>(y_norm + tok * K + chunk_off(j));
-          dst[0] = u32x4{wd[j][0], wd[j][1], wd[j][2], wd[j][3]};
-          dst[1] = u32x4{wd[j][4], wd[j][5], wd[j][6], wd[j][7]};
+          dst[0] = u32x4{p[0], p[1], p[2], p[3]};
+          dst[1] = u32x4{p[4], p[5], p[6], p[7]};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {  // the bit-0 butterfly
+          v[j][2 * i] = y[2 * i] + y[2 * i + 1];
+          v[j][2 * i + 1] = y[2 * i] - y[2 * i + 1];
         }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {  // unpack a bf16 pair and do the bit-0 butterfly
+          const uint32_t w = raw[j][i >> 2][i & 3];
+          const float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xffff0000u);
+          v[j][2 * i] = lo + hi;
+          v[j][2 * i + 1] = lo - hi;
+        }
     }
-
-    float v[C][16];
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {  // unpack a bf16 pair and do the bit-0 butterfly
-        const float lo = __uint_as_float(wd[j][i] << 16), hi = __uint_as_float(wd[j][i] & 0xffff0000u);
-        v[j][2 * i] = lo + hi;
-        v[j][2 * i + 1] = lo - hi;
-      }
 
     float amax = 0.f;
 #pragma unroll
@@ -319,6 +341,19 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_g256_kernel(const uint1
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + chunk_off(j)));
       }
     }
+  };
+
+  u32x4 raw[C][2];
+  if constexpr (WALK) {
+    const int64_t stride = int64_t(gridDim.x) * kWaves;
+    for (int64_t tok = int64_t(blockIdx.x) * kWaves + wave; tok < M; tok += stride) {  // uniform per wave
+      load(raw, tok);
+      process(raw, tok);
+    }
+  } else {
+    const int64_t tok = int64_t(blockIdx.x) * P + wave / TW;
+    load(raw, tok);
+    process(raw, tok);
   }
 }
 
@@ -343,6 +378,51 @@ hipError_t launch(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs
   return hipSuccess;
 }
 
+// Workgroups of the walking fused-norm kernel that the current device runs
+// at once (compute units x resident workgroups per unit).  A read-only fact
+// of the device, worked out once per device (the first call with that
+// device current; later calls from any host thread only read it); 0 on
+// error.
+template <int C>
+int walk_slots() {
+  constexpr int kDevices = 64;
+  static std::once_flag once[kDevices];
+  static int slots[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  auto query = [](int d) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(rotate_quant_g256_kernel<C, 1, true, true>), kThreads, 0) !=
+        hipSuccess)
+      return 0;
+    return cus * (per_cu > 0 ? per_cu : 1);
+  };
+  if (dev >= kDevices) return query(dev);  // not memoised
+  std::call_once(once[dev], [&] { slots[dev] = query(dev); });
+  return slots[dev];
+}
+
+// The fused norm pass with one wave per token and no bf16 norm output, on
+// the resident grid: each workgroup fills the norm factors once and then
+// walks its tokens (same-box A/B, M 8704, K 4096: 26.7 -> 25.0 us, 26.0 ->
+// 23.8 us on another box; M 20000: 54.6 -> 51.2 us).  With the norm output
+// the walk measured slower at M 20000 (81.2 -> 85.1 us), so that case keeps
+// one workgroup per four tokens.
+template <int C>
+hipError_t launch_walk(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w,
+                       float eps, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const int slots = walk_slots<C>();
+  if (slots <= 0) return hipErrorInvalidValue;
+  const int64_t need = (M + kWaves - 1) / kWaves;
+  const unsigned grid = unsigned(need < slots ? need : slots);
+  hipLaunchKernelGGL((rotate_quant_g256_kernel<C, 1, true, true>), dim3(grid), dim3(kThreads), 0, stream, x, M,
+                     int(K), xq, xs, norm_w, eps, nullptr);
+  return hipGetLastError();
+}
+
 template <int C, int TW, bool NORM>
 hipError_t launch_split(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* xs, const float* norm_w,
                         float eps, uint16_t* y_norm, hipStream_t stream) {
@@ -352,6 +432,9 @@ hipError_t launch_split(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, flo
   // 4.20 us, M 2048 8.40 -> 7.96 us; M 8704 is 4 % faster unsplit).
   if constexpr (C % 2 == 0 && TW < 4) {
     if (M < 4096) return launch<C / 2, 2 * TW, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
+  }
+  if constexpr (NORM && TW == 1) {
+    if (M >= 4096 && y_norm == nullptr) return launch_walk<C>(x, M, K, xq, xs, norm_w, eps, stream);
   }
   return launch<C, TW, NORM>(x, M, K, xq, xs, norm_w, eps, y_norm, stream);
 }
