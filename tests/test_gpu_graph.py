@@ -72,3 +72,33 @@ def test_linear_multi_graph_replays(lib):
             assert torch.equal(y.view(torch.int16), ye.view(torch.int16)), f"replay {rep}"
         run()  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_rmsnorm_token_walk_graph_replays(lib):
+    """The fused norm call without the bf16 output at 4100 tokens, K 4096
+    (the workgroups walk the tokens on the resident grid), captured alone:
+    codes and scales of every replay equal the eager call's."""
+    import torch
+    M, K = 4100, 4096
+    say(f"rmsnorm_rotate_quant (token walk) in a HIP graph M={M} K={K}")
+    x = bf16_to_dev(wl.make_activations(M, K, K // 100, seed=11))
+    nw = to_dev(wl.make_norm_weight(K, K // 100, seed=11))
+    q_eager, s_eager = lib.rmsnorm_rotate_quant(x, nw)
+    q = torch.empty_like(q_eager)
+    s = torch.empty_like(s_eager)
+    rc = lib.convrot_rmsnorm_rotate_quant(x, nw, 1e-6, M, K, 256, q, s, None)  # first call outside the capture
+    assert rc == 0
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lib.convrot_rmsnorm_rotate_quant(x, nw, 1e-6, M, K, 256, q, s, None)
+    for rep in range(3):
+        q.zero_()
+        s.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, q_eager), f"replay {rep}"
+        assert torch.equal(s, s_eager), f"replay {rep}"
+        lib.rmsnorm_rotate_quant(x, nw)  # eager work between replays
+        torch.cuda.synchronize()
