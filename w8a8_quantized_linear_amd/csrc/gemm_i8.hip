@@ -751,12 +751,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_k64_kernel(const int8_t
 // With two waves per SIMD each wave reads one K-slice's fragments at a time
 // (one register set: 192 accumulators leave no room for a second), and the
 // other wave's MFMAs cover the LDS latency.  One barrier per 128-K step: the
-// loads of stage kt + 1 go out at the start of step kt into the buffer the
-// previous barrier freed, and are waited for at its end.  The last step is
-// peeled: instead of a stage it loads the tile's scales (int8 only) into
-// the buffer it does not read, where the epilogue finds them.  One
-// workgroup per tile; the plan is chosen where such tiles fill whole rounds
-// of the CUs.
+// loads of stage kt + 1 go out during step kt, right after its first LDS
+// reads, into the buffer the previous barrier freed, and are waited for at
+// its end; the prologue sends stages 0 and 1.  The last step is peeled:
+// instead of a stage it loads the tile's scales (int8 only) into the
+// buffer it does not read, where the epilogue finds them.  One workgroup
+// per tile; the plan is chosen where such tiles fill whole rounds of the
+// CUs.  Under sustained load the main loop runs at the device's power
+// limit: a schedule with fewer idle MFMA cycles runs at a lower clock
+// (rocprofv3 counters: MFMA-busy times clock stays at 1.32-1.34 GHz), so
+// what pays is less work around each tile and fewer bytes per MFMA.
 constexpr int kW8Threads = 512;
 constexpr int kW8BM = 256, kW8BN = 384;
 constexpr int kW8GroupM = 8;  // M-tiles per block of the tile order
