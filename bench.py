@@ -689,14 +689,14 @@ def copy_peak(torch, timer):
 # GEMM shapes whose tile plans the counter runs cover (M, N, K, weight bits).
 # int8 weights: the headline shape (256x384, eight waves), M=2048, N=6144
 # (256x192), the MLP down shape (256x128, three stages), the attention shape
-# M=512 (64x128, four stages) and M=6144, N=12288 (256x256).  int4 weights:
+# M=512 (64x128, four stages) and M=6144, N=8192 (256x256).  int4 weights:
 # M=2048, N=12288 (256x192), the MLP down shape, M=512 and M=4096, N=12288
 # (256x256).  Each plan also runs at a second K, so that counts which grow
 # with K (the main loop) separate from those which do not (set-up and
 # epilogue).
 GEMM_TILE_SHAPES = [(2048, 12288, 4096, 8), (2048, 12288, 8192, 8), (2048, 6144, 4096, 8), (2048, 6144, 8192, 8),
                     (2048, 4096, 12288, 8), (2048, 4096, 4096, 8), (512, 4096, 4096, 8), (512, 4096, 8192, 8),
-                    (6144, 12288, 4096, 8), (6144, 12288, 8192, 8),
+                    (6144, 8192, 4096, 8), (6144, 8192, 8192, 8),
                     (2048, 12288, 4096, 4), (2048, 12288, 8192, 4), (2048, 4096, 12288, 4), (2048, 4096, 4096, 4),
                     (512, 4096, 4096, 4), (512, 4096, 8192, 4), (4096, 12288, 4096, 4), (4096, 12288, 8192, 4)]
 

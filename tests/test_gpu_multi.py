@@ -1,5 +1,6 @@
 """GPU parity of the multi-output calls (several weight matrices sharing one
-quantized input, one GEMM launch) against the oracle and against the
+quantized input; one GEMM launch, or one per output where every output
+takes the eight-wave tiles) against the oracle and against the
 single-output calls, through the C ABI."""
 import numpy as np
 import pytest
@@ -37,6 +38,9 @@ def _weights(rng, Ns, K, wbits):
     (8, 2048, 512, (4096, 1024, 1024)),       # 128x128 tiles across three outputs (short K)
     (8, 2048, 256, (12288, 12288)),           # 256x256 tiles (every N a multiple of 256)
     (8, 2048, 2048, (2048, 1024, 1024)),      # 256x128 tiles, three stages, one per CU
+    (8, 2048, 2048, (12288, 12288)),          # every output on eight-wave 256x384 tiles, one launch each
+    (8, 8704, 2048, (12288, 12288)),          # each output: eight-wave tiles on 8192 rows, then the last 512
+    (8, 2048, 2048, (12288, 4096)),           # one output cannot take eight-wave tiles: one multi launch
     (4, 64, 1024, (512, 96, 1000)),           # packed int4
     (4, 4096, 256, (6144, 6144)),             # packed int4, 256x256
 ])

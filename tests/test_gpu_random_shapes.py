@@ -34,6 +34,9 @@ SHAPES = [
     (8, 1920, 12288, 2048),   # 256x384, eight waves: one round, ragged M
     (8, 4000, 12288, 4096),   # 256x384, eight waves: two rounds, ragged M
     (8, 1024, 24576, 2048),   # 256x384, eight waves
+    (8, 6000, 12288, 2048),   # 256x384, eight waves: three whole rounds, ragged M
+    (8, 8704, 12288, 2048),   # 256x384 on rows 0..8191 (four rounds), the last 512 rows on the ordinary plan
+    (8, 7000, 12288, 2048),   # 256x384 on rows 0..6143 (three rounds), 856 ragged rows on the ordinary plan
     (4, 2048, 12288, 4096),   # 256x192, packed int4
     (4, 3900, 12288, 2048),   # 256x256, packed int4, ragged M
 ]

@@ -1222,6 +1222,27 @@ bool w8_whole_rounds(int64_t M, int64_t K, const GemmOutDesc* d, int n, int max_
   return tiles % cus == 0 && tiles <= max_rounds * cus;
 }
 
+// Rows of M that one output (int8 weights) gives to the eight-wave tiles:
+// all of them where its tiles make whole rounds of the CUs; otherwise,
+// where two or more whole rounds fit, the longest run of whole token tiles
+// whose tiles fill whole rounds, the remaining rows (less than a round's
+// worth of tiles) taking the ordinary plan in a second launch; else none.
+// A partial round of these tiles, with no second tile per CU to overlap
+// their epilogues, measured slower than the ordinary plan (same-box A/B,
+// bit-identical output, K 4096, N 12288: M 8704, 4.25 rounds, 361 us, and
+// 355-361 us on 256x256 tiles, against 338 us with 8192 rows on eight-wave
+// tiles and 512 on the ordinary plan; M 6144, three whole rounds, 232 us
+// against 252 us on 256x256).
+int64_t w8_rows(int64_t M, int64_t K, const GemmOutDesc& d) {
+  if (K % 256 != 0 || d.N % kW8BN != 0 || K / 128 < 16) return 0;
+  const int64_t cus = device_cus(), tn = d.N / kW8BN, tm = (M + kW8BM - 1) / kW8BM;
+  if ((tm * tn) % cus == 0) return M;
+  int64_t per_round = 1;  // token tiles whose tiles fill whole rounds
+  while ((per_round * tn) % cus != 0) ++per_round;
+  const int64_t m0 = (M / kW8BM) / per_round * per_round;
+  return m0 * tn >= 2 * cus ? m0 * kW8BM : 0;
+}
+
 // Tuning builds only (-DCONVROT_TUNING):
 // CONVROT_GEMM_PLAN=<BM>x<BN>[:<cols>][,<BM>x<BN>] forces a plan for a single
 // output, for sweeps (every plan gives bit-identical results).
@@ -1288,7 +1309,28 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     return hipSuccess;
   }
   const TileChoice forced = tile_override();
-  if (!W4 && !forced.bm && w8_whole_rounds(M, K, d, n)) return launch_w8(xq, x_scale, M, K, d[0], stream);
+  if (!W4 && !forced.bm) {
+    // Eight-wave tiles (w8_rows) for every output, or for none: outputs
+    // that all qualify run one after the other, each in its own launches.
+    int64_t rows[kMaxOuts];
+    bool all = true;
+    for (int o = 0; o < n; ++o) all = all && (rows[o] = w8_rows(M, K, d[o])) > 0;
+    if (all) {
+      for (int o = 0; o < n; ++o) {
+        const int r = int(rows[o]);
+        hipError_t e = launch_w8(xq, x_scale, r, K, d[o], stream);
+        if (e == hipSuccess && r < M) {
+          const GemmOutDesc rest{d[o].wq, d[o].w_scale, d[o].N, d[o].ldy,
+                                 d[o].acc ? d[o].acc + int64_t(r) * d[o].ldy : nullptr,
+                                 d[o].y ? d[o].y + int64_t(r) * d[o].ldy : nullptr};
+          const TileChoice tc = choose_tile(M - r, (int64_t(K) + 127) / 128, &rest, 1);
+          e = launch_tile<W4>(tc, xq + int64_t(r) * K, x_scale ? x_scale + r : nullptr, M - r, K, &rest, 1, stream);
+        }
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
   const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
   return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
