@@ -14,8 +14,11 @@ pytestmark = pytest.mark.gpu
 
 
 # Headline shape (eight-wave 256x384 tiles), a small one (64x128 tiles,
-# four stages) and a long-K one (256x128 tiles, three stages).
-@pytest.mark.parametrize("M,K,N", [(2048, 4096, 12288), (512, 4096, 4096), (2048, 12288, 4096)])
+# four stages), a long-K one (256x128 tiles, three stages), and the decoder
+# stack's gate/up shape, whose GEMM is two launches (eight-wave tiles on the
+# first 8192 rows, the ordinary plan on the last 512).
+@pytest.mark.parametrize("M,K,N", [(2048, 4096, 12288), (512, 4096, 4096), (2048, 12288, 4096),
+                                   (8704, 2048, 12288)])
 def test_w8a8_linear_graph_replays(lib, M, K, N):
     import torch
     say(f"w8a8_linear in a HIP graph M={M} K={K} N={N}")

@@ -77,10 +77,11 @@ def test_gemm_irregular_shapes(lib, wbits, M, N, K):
     assert np.array_equal(yh[GUARD:GUARD + M * N].reshape(M, N)[rows].view(np.uint16), yref)
 
 
-@pytest.mark.parametrize("M,N,K", [(1920, 12288, 2048), (2048, 12288, 4096)])
+@pytest.mark.parametrize("M,N,K", [(1920, 12288, 2048), (2048, 12288, 4096), (8704, 12288, 2048)])
 def test_gemm_eight_wave_single_outputs(lib, M, N, K):
-    """The eight-wave 256x384 plan asked for the int32 accumulators alone and
-    for the bf16 output alone: each equal to the same launch with both."""
+    """The eight-wave 256x384 plan (at M 8704: on the first 8192 rows, the
+    ordinary plan on the rest) asked for the int32 accumulators alone and
+    for the bf16 output alone: each equal to the same call with both."""
     import torch
     say(f"gemm_i8 eight-wave single outputs M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N + K)
