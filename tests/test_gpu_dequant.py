@@ -131,11 +131,14 @@ def test_dequant_path_is_closer_to_full_precision(lib):
 
 
 @pytest.mark.parametrize("M,N,K", [(4100, 12288, 528), (3000, 7000, 1504), (2000, 4000, 3008), (300, 3000, 2000),
-                                   (1000, 4000, 1008), (3000, 3000, 608), (1920, 12288, 1024), (1800, 12288, 2048)])
+                                   (1000, 4000, 1008), (3000, 3000, 608), (1920, 12288, 1024), (1800, 12288, 2048),
+                                   (6000, 12288, 1024), (8704, 12288, 1024)])
 def test_gemm_bf16_irregular_guarded(lib, M, N, K):
     """Irregular shapes on every tile plan of the bf16 matmul (256x256,
     256x192, 256x128 three-stage, 64x128 and 128x128 four-stage, 128x128,
-    and the eight-wave 256x384 tiles, one round with ragged M):
+    and the eight-wave 256x384 tiles: one round and three whole rounds with
+    ragged M, and on the first 8192 of 8704 rows with the ordinary plan on
+    the rest):
     sampled rows within the accumulation bound of the oracle, and guard
     words around the output untouched."""
     import torch

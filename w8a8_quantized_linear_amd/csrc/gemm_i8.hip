@@ -1209,30 +1209,19 @@ TileChoice choose_tile(int64_t M, int64_t ksteps, const GemmOutDesc* d, int n) {
   return {128, 128};
 }
 
-// The eight-wave 256x384 plan (int8 weights, one output), where its tiles
-// make one or two whole rounds of the CUs and K has at least 16 stages:
-// M 2048, K 4096, N 12288 (256 tiles) 95.7 -> 87.2 us against 256x192,
-// K 8192 182.6 -> 167.8 us; M 4096 (two rounds) 176.2 -> 173.8 us against
-// 256x256 (same box, interleaved, bit-identical outputs).  It takes one tile
-// per workgroup, so a partial last round would leave CUs idle.
-bool w8_whole_rounds(int64_t M, int64_t K, const GemmOutDesc* d, int n, int max_rounds = 2) {
-  if (!w8_fits(K, d, n) || K / 128 < 16) return false;
-  const int64_t cus = device_cus();
-  const int64_t tiles = ((M + kW8BM - 1) / kW8BM) * (d[0].N / kW8BN);
-  return tiles % cus == 0 && tiles <= max_rounds * cus;
-}
-
-// Rows of M that one output (int8 weights) gives to the eight-wave tiles:
-// all of them where its tiles make whole rounds of the CUs; otherwise,
-// where two or more whole rounds fit, the longest run of whole token tiles
-// whose tiles fill whole rounds, the remaining rows (less than a round's
-// worth of tiles) taking the ordinary plan in a second launch; else none.
-// A partial round of these tiles, with no second tile per CU to overlap
-// their epilogues, measured slower than the ordinary plan (same-box A/B,
-// bit-identical output, K 4096, N 12288: M 8704, 4.25 rounds, 361 us, and
-// 355-361 us on 256x256 tiles, against 338 us with 8192 rows on eight-wave
-// tiles and 512 on the ordinary plan; M 6144, three whole rounds, 232 us
-// against 252 us on 256x256).
+// Rows of M that one output gives to the eight-wave 256x384 tiles (int8
+// weights; the bf16 matmul with K in bytes), which take one tile per
+// workgroup and need K to have at least 16 stages: all of them where the
+// tiles make whole rounds of the CUs; otherwise, where two or more whole
+// rounds fit, the longest run of whole token tiles whose tiles fill whole
+// rounds, the remaining rows (less than a round's worth of tiles) planned
+// as a GEMM of their own in a second launch; else none.  Same box,
+// interleaved, bit-identical outputs: M 2048, K 4096, N 12288 (one round)
+// 95.7 -> 87.2 us against 256x192; M 4096 (two rounds) 176.2 -> 173.8 us
+// and M 6144 (three) 252 -> 232 us against 256x256.  A partial round, with
+// no second tile per CU to overlap the last tiles' epilogues, gains
+// nothing: M 8704 (4.25 rounds) 361 us in one launch, 355-361 us on 256x256
+// tiles, 338 us with 8192 rows on these tiles and 512 on the ordinary plan.
 int64_t w8_rows(int64_t M, int64_t K, const GemmOutDesc& d) {
   if (K % 256 != 0 || d.N % kW8BN != 0 || K / 128 < 16) return 0;
   const int64_t cus = device_cus(), tn = d.N / kW8BN, tm = (M + kW8BM - 1) / kW8BM;
@@ -1366,16 +1355,20 @@ hipError_t launch_gemm_bf16(const uint16_t* x, const uint16_t* w, int64_t M, int
                             hipStream_t stream) {
   const GemmOutDesc d{w, nullptr, int(N), int(N), nullptr, y};
   const TileChoice forced = tile_override();
-  // Eight-wave 256x384 tiles where they make exactly one round (K in
-  // bytes): M 2048, K 4096, N 12288 174.8 -> 161.2 us (same box,
-  // interleaved, identical outputs); at two rounds (M 4096) 256x256 stays
-  // ahead, 309.8 against 312.0 us.
-  if (!forced.bm && w8_whole_rounds(M, 2 * K, &d, 1, 1)) {
+  // Eight-wave 256x384 tiles on the rows w8_rows gives them (K in bytes),
+  // the rest planned as a GEMM of its own.  Same box, interleaved,
+  // identical outputs: M 2048, K 4096, N 12288 (one round) 174.8 -> 161.2 us
+  // against 256x192; M 6144 (three rounds) 471.8 -> 454.2 us against
+  // 256x256; M 4096 and M 8704 within 0.4 % of 256x256.
+  const int64_t w8r = forced.bm ? 0 : w8_rows(M, 2 * K, d);
+  if (w8r > 0) {
     const GemmOut o{reinterpret_cast<const uint8_t*>(w), nullptr, nullptr, y, int(N), int(N)};
-    const int tiles_m = int((M + kW8BM - 1) / kW8BM), tiles_n = int(N / kW8BN);
+    const int tiles_m = int((w8r + kW8BM - 1) / kW8BM), tiles_n = int(N / kW8BN);
     hipLaunchKernelGGL(gemm_bf16_w8_kernel, dim3(unsigned(int64_t(tiles_m) * tiles_n)), dim3(kW8Threads), 0, stream,
-                       reinterpret_cast<const int8_t*>(x), int(M), int(2 * K), tiles_m, tiles_n, o);
-    return hipGetLastError();
+                       reinterpret_cast<const int8_t*>(x), int(w8r), int(2 * K), tiles_m, tiles_n, o);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || w8r == M) return e;
+    return launch_gemm_bf16(x + w8r * K, w, M - w8r, N, K, y + w8r * N, stream);
   }
   const TileChoice tc = forced.bm ? forced : choose_tile(M, (2 * K + 127) / 128, &d, 1);
   if (tc.ns == 3 && tc.bm == 256 && tc.bn == 128) return launch_bf16<256, 128, 3>(x, w, int(M), int(N), int(K), y, stream);
