@@ -523,14 +523,32 @@ def extras_vision(torch, cr, wl, timer):
     return res
 
 
+def _stream_probe():
+    """The same-bytes streaming helper (tests/gpu_probe/stream_rq.hip, built
+    by __graft_entry__.build), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "tests", "gpu_probe", "libstream_rq.so")
+    if not os.path.exists(path):
+        return None
+    fn = ctypes.CDLL(path).stream_rq_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
 def rq_passes(torch, cr, timer):
     """Rotate-quantize bandwidth on the large passes, each cycled through
     enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16).  Beside
-    each, a plain streaming pass over the same input buffers: torch's
-    vectorized elementwise kernel (x + 0 on the bf16 bits read as int32
-    words) into a buffer of the same size, 2 bytes read and 2 written per
-    value with no arithmetic: the rate a plain elementwise kernel reaches at
-    that size."""
+    each, two plain streaming passes over the same input buffers:
+    - torch's vectorized elementwise kernel (x + 0 on the bf16 bits read as
+      int32 words) into a buffer of the same size, 2 bytes read and 2
+      written per value with no arithmetic: the rate a plain elementwise
+      kernel reaches at that size;
+    - the same-bytes helper (tests/gpu_probe/stream_rq.hip): exactly the
+      pass's 3K + 4 bytes per row, 16-byte nontemporal loads and stores as in
+      the quantizer, no arithmetic, one 16-value chunk per thread or a
+      resident grid walking the chunks; the faster of the two is reported."""
     dev = torch.device("cuda")
     res = []
     for (m, k) in RQ_PASSES:
@@ -545,11 +563,35 @@ def rq_passes(torch, cr, timer):
         ys = [torch.empty((m, k // 2), dtype=torch.int32, device=dev) for _ in range(n)]
         t_ref = timer.time(lambda i: torch.add(xs[i % n].view(torch.int32), 0, out=ys[i % n]), 200, warm=50)
         ref_bytes = 4 * m * k
-        res.append({"M": m, "K": k, "us": round(t * 1e6, 2), "bytes": per,
-                    "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4),
-                    "elementwise_same_input": {"us": round(t_ref * 1e6, 2), "bytes": ref_bytes,
-                                               "achieved": round(ref_bytes / t_ref / 1e9, 1)}})
-        del xs, ys
+        rec = {"M": m, "K": k, "us": round(t * 1e6, 2), "bytes": per,
+               "achieved": round(per / t / 1e9, 1), "frac": round(per / t / 1e9 / PEAK_HBM_GBS, 4),
+               "elementwise_same_input": {"us": round(t_ref * 1e6, 2), "bytes": ref_bytes,
+                                          "achieved": round(ref_bytes / t_ref / 1e9, 1)}}
+        del ys
+        probe = _stream_probe()
+        if probe is not None:
+            qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
+            ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
+            blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+            stream = torch.cuda.current_stream().cuda_stream
+
+            def sweep(mode):
+                def run(i):
+                    rc = probe(xs[i % n].data_ptr(), qs[i % n].data_ptr(), ss[i % n].data_ptr(), m, k, mode, blocks,
+                               stream)
+                    if rc:
+                        raise RuntimeError(f"stream_rq_launch: {rc}")
+                return timer.time(run, 200, warm=50)
+
+            ts = {"chunk_per_thread": sweep(0), f"resident_grid_{blocks}": sweep(1)}
+            best = min(ts, key=ts.get)
+            rec["stream_same_bytes"] = {"us": round(ts[best] * 1e6, 2), "bytes": per, "shape": best,
+                                        "achieved": round(per / ts[best] / 1e9, 1),
+                                        "frac": round(per / ts[best] / 1e9 / PEAK_HBM_GBS, 4),
+                                        "us_by_shape": {a: round(b * 1e6, 2) for a, b in ts.items()}}
+            del qs, ss
+        res.append(rec)
+        del xs
     return res
 
 

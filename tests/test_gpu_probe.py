@@ -13,6 +13,7 @@ LIB = os.path.join(HERE, "gpu_probe", "libmfma_rate.so")
 def _lib():
     if not os.path.exists(LIB):
         pytest.skip("tests/gpu_probe/libmfma_rate.so not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  (torch's HIP runtime must be the process's: see the binding's load())
     lib = ctypes.CDLL(LIB)
     for fn in (lib.mfma_rate_launch, lib.mfma_rate_launch_bf16):
         fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
@@ -67,3 +68,47 @@ def test_probe_bf16_loop_accumulates():
         sums.append(out.view(torch.float32).double().clone())
     assert torch.isfinite(sums[1]).all() and (sums[0] > 0).all()
     assert torch.allclose(sums[1], 2 * sums[0], rtol=1e-5)
+
+
+STREAM = os.path.join(HERE, "gpu_probe", "libstream_rq.so")
+
+
+def _stream():
+    if not os.path.exists(STREAM):
+        pytest.skip("tests/gpu_probe/libstream_rq.so not built (run __graft_entry__.build())")
+    import torch  # noqa: F401  (as in _lib)
+    fn = ctypes.CDLL(STREAM).stream_rq_launch
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                   ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    return fn
+
+
+def test_stream_probe_rejects_bad_arguments():
+    fn = _stream()
+    p = ctypes.c_void_p(0x1000)
+    assert fn(None, p, p, 4, 256, 0, 8, None) == 1
+    assert fn(p, p, p, 0, 256, 0, 8, None) == 1
+    assert fn(p, p, p, 4, 250, 0, 8, None) == 1      # K not a multiple of 16
+    assert fn(p, p, p, 4, 256, 2, 8, None) == 1      # no such mode
+    assert fn(p, p, p, 4, 256, 1, 0, None) == 1      # empty grid
+    assert fn(ctypes.c_void_p(0x1008), p, p, 4, 256, 0, 8, None) == 1  # misaligned
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("mode", [0, 1])
+def test_stream_probe_moves_every_byte(mode):
+    """Both launch shapes write the high byte of every bf16 word and one word
+    per row: the probe really reads all of its input."""
+    import torch
+    fn = _stream()
+    M, K = 37, 4096 + 256
+    x = torch.randint(-32768, 32768, (M, K), dtype=torch.int32, device="cuda").to(torch.int16)
+    q = torch.zeros((M, K), dtype=torch.uint8, device="cuda")
+    v = torch.zeros((M,), dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    assert fn(x.data_ptr(), q.data_ptr(), v.data_ptr(), M, K, mode, 5, stream) == 0
+    torch.cuda.synchronize()
+    expect = ((x.to(torch.int32) >> 8) & 0xff).to(torch.uint8)
+    assert torch.equal(q, expect)
+    assert torch.equal(v, torch.ones_like(v))

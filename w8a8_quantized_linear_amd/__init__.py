@@ -63,6 +63,13 @@ def load():
         raise RuntimeError(
             f"{_LIB_PATH} is not built; run `python -m w8a8_quantized_linear_amd.build` "
             "(or __graft_entry__.build()) first")
+    # torch first, where it is installed: it bundles its own HIP runtime
+    # under the same soname as ROCm's, so whichever loads first serves the
+    # process; loading this library first would put torch on ROCm's copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64, I, SZ, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
     sigs = {
