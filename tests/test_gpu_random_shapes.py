@@ -99,3 +99,24 @@ def test_gemm_eight_wave_single_outputs(lib, M, N, K):
     torch.cuda.synchronize()
     assert torch.equal(acc_only, acc_both)
     assert torch.equal(y_only, y_both)
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 12288, 2048), (8704, 12288, 2048)])
+def test_gemm_eight_wave_accumulators_without_scales(lib, M, N, K):
+    """The eight-wave plan (one round; and on the first 8192 of 8704 rows)
+    asked for the int32 accumulators alone with no scales at all (null
+    pointers, which the call allows when it writes no bf16 output): the same
+    accumulators as a call that passes scales."""
+    import torch
+    say(f"gemm_i8 eight-wave accumulators without scales M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 2 * N + K)
+    a = to_dev(rng.integers(-127, 128, (M, K), dtype=np.int8))
+    b = to_dev(rng.integers(-127, 128, (N, K), dtype=np.int8))
+    xs = to_dev((rng.random(M) * 0.1 + 1e-3).astype(np.float32))
+    ws = to_dev((rng.random(N) * 1e-3 + 1e-5).astype(np.float32))
+    acc_ref = torch.empty((M, N), dtype=torch.int32, device="cuda")
+    acc = torch.full((M, N), 7, dtype=torch.int32, device="cuda")
+    assert lib.convrot_gemm_i8(a, xs, b, 8, ws, M, N, K, acc_ref, None) == 0
+    assert lib.convrot_gemm_i8(a, None, b, 8, None, M, N, K, acc, None) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(acc, acc_ref)

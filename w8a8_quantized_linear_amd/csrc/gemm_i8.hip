@@ -834,8 +834,10 @@ __device__ __forceinline__ void gemm_w8_body(const int8_t* __restrict__ X, const
   };
   // Weight scales (384 floats, waves 0 and 1) at byte 0 of sW0 and token
   // scales (256 floats, wave 2; rows past M read as zero) at byte 2048.
+  // Only the bf16 output needs them: a call for the int32 accumulators
+  // alone may pass no scales (null pointers), so nothing is read then.
   auto load_scales = [&]() {
-    if (wave < 3) {
+    if (out.y && wave < 3) {
       const float* src = wave < 2 ? out.sw + n0 + 256 * wave : sx + m0;
       const int nrec = wave == 0 ? 1024 : (wave == 1 ? 4 * (BN - 256) : 4 * rows_x);
       const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(src), short(0), nrec,
