@@ -537,6 +537,36 @@ def _stream_probe():
     return fn
 
 
+def stream_same_bytes(torch, xs, m, k, timer):
+    """The same-bytes streaming helper over the input buffers xs (bf16
+    [m, k] each, cycled), into output buffers of its own: the faster of its
+    two launch shapes, or None when the helper is not built."""
+    probe = _stream_probe()
+    if probe is None:
+        return None
+    dev = torch.device("cuda")
+    n = len(xs)
+    per = m * (3 * k + 4)
+    qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
+    ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
+    blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def sweep(mode):
+        def run(i):
+            rc = probe(xs[i % n].data_ptr(), qs[i % n].data_ptr(), ss[i % n].data_ptr(), m, k, mode, blocks, stream)
+            if rc:
+                raise RuntimeError(f"stream_rq_launch: {rc}")
+        return timer.time(run, 200, warm=50)
+
+    ts = {"chunk_per_thread": sweep(0), f"resident_grid_{blocks}": sweep(1)}
+    best = min(ts, key=ts.get)
+    del qs, ss
+    return {"us": round(ts[best] * 1e6, 2), "bytes": per, "shape": best,
+            "achieved": round(per / ts[best] / 1e9, 1), "frac": round(per / ts[best] / 1e9 / PEAK_HBM_GBS, 4),
+            "us_by_shape": {a: round(b * 1e6, 2) for a, b in ts.items()}}
+
+
 def rq_passes(torch, cr, timer):
     """Rotate-quantize bandwidth on the large passes, each cycled through
     enough buffer sets to exceed 2x the MALL (inputs N(0,1) bf16).  Beside
@@ -568,28 +598,9 @@ def rq_passes(torch, cr, timer):
                "elementwise_same_input": {"us": round(t_ref * 1e6, 2), "bytes": ref_bytes,
                                           "achieved": round(ref_bytes / t_ref / 1e9, 1)}}
         del ys
-        probe = _stream_probe()
-        if probe is not None:
-            qs = [torch.empty((m, k), dtype=torch.int8, device=dev) for _ in range(n)]
-            ss = [torch.empty((m,), dtype=torch.float32, device=dev) for _ in range(n)]
-            blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
-            stream = torch.cuda.current_stream().cuda_stream
-
-            def sweep(mode):
-                def run(i):
-                    rc = probe(xs[i % n].data_ptr(), qs[i % n].data_ptr(), ss[i % n].data_ptr(), m, k, mode, blocks,
-                               stream)
-                    if rc:
-                        raise RuntimeError(f"stream_rq_launch: {rc}")
-                return timer.time(run, 200, warm=50)
-
-            ts = {"chunk_per_thread": sweep(0), f"resident_grid_{blocks}": sweep(1)}
-            best = min(ts, key=ts.get)
-            rec["stream_same_bytes"] = {"us": round(ts[best] * 1e6, 2), "bytes": per, "shape": best,
-                                        "achieved": round(per / ts[best] / 1e9, 1),
-                                        "frac": round(per / ts[best] / 1e9 / PEAK_HBM_GBS, 4),
-                                        "us_by_shape": {a: round(b * 1e6, 2) for a, b in ts.items()}}
-            del qs, ss
+        same = stream_same_bytes(torch, xs, m, k, timer)
+        if same is not None:
+            rec["stream_same_bytes"] = same
         res.append(rec)
         del xs
     return res
@@ -909,6 +920,8 @@ def main():
     gemm_tops = ops / t_gemm / 1e12
     rq_bytes = M * (3 * K + 4)
     rq_gbs = rq_bytes / t_rq / 1e9
+    # the same bytes moved by a plain streaming pass over the same inputs
+    rq_same = stream_same_bytes(torch, [s[0] for s in sets], M, K, timer)
 
     # The headline: W untimed warm-up steps, then exactly K timed steps.
     for i in range(args.warmup):
@@ -995,6 +1008,7 @@ def main():
             "avg_launch_us": round(t_rq * 1e6, 3),
             "algorithmic_bytes_per_launch": rq_bytes,
             "traffic": load_traffic("rotate_quant_C3u", RQ_SOURCES),
+            "stream_same_bytes": rq_same,
         },
         "parity": parity,
         "device": device_info(torch),
