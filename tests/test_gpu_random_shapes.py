@@ -16,6 +16,8 @@ SHAPES = [
     (8, 6000, 8448, 1040),    # 256x256
     (4, 4100, 12288, 2080),   # 256x256, packed int4
     (8, 4211, 3840, 5904),    # 256x192
+    (8, 8704, 4096, 2048),    # 256x256 on rows 0..8191 (two rounds), the last 512 rows on the ordinary plan
+    (8, 8700, 4096, 2048),    # the same with 508 ragged rows after the two rounds
     (4, 3973, 6684, 3136),    # 256x192, packed int4
     (4, 1806, 4864, 5088),    # 256x192, packed int4
     (8, 1916, 3894, 7504),    # 256x128, three stages

@@ -1323,6 +1323,28 @@ hipError_t launch_plan(const int8_t* xq, const float* x_scale, int M, int K, con
     }
   }
   const TileChoice tc = forced.bm ? forced : choose_tile(M, (int64_t(K) + 127) / 128, d, n);
+  // Where the planner takes persistent 256x192 tiles for int8 weights and
+  // 256x256 tiles would fill two or more whole rounds of the CUs on the
+  // first rows, those rows take 256x256 tiles and the rest are planned as
+  // a GEMM of their own (same-box A/B, bit-identical output, M 8704, N 4096:
+  // K 12288 393-398 -> 364 us, K 4096 141 -> 131 us; 256x256 tiles fill
+  // 2.1 rounds there).
+  if (!W4 && !forced.bm && n == 1 && tc.bm == 256 && tc.bn == 192 && d[0].N % 256 == 0 && K / 128 >= 16) {
+    const int64_t cus = device_cus(), tn = d[0].N / 256;
+    int64_t per_round = 1;  // token tiles whose tiles fill whole rounds
+    while ((per_round * tn) % cus != 0) ++per_round;
+    const int64_t m0 = (M / 256) / per_round * per_round;
+    if (m0 * tn >= 2 * cus) {
+      const int r = int(m0 * 256);
+      const hipError_t e = launch_tile<W4>(TileChoice{256, 256}, xq, x_scale, r, K, d, 1, stream);
+      if (e != hipSuccess || r == M) return e;
+      const GemmOutDesc rest{d[0].wq, d[0].w_scale, d[0].N, d[0].ldy,
+                             d[0].acc ? d[0].acc + int64_t(r) * d[0].ldy : nullptr,
+                             d[0].y ? d[0].y + int64_t(r) * d[0].ldy : nullptr};
+      const TileChoice tr = choose_tile(M - r, (int64_t(K) + 127) / 128, &rest, 1);
+      return launch_tile<W4>(tr, xq + int64_t(r) * K, x_scale ? x_scale + r : nullptr, M - r, K, &rest, 1, stream);
+    }
+  }
   return launch_tile<W4>(tc, xq, x_scale, M, K, d, n, stream);
 }
 
